@@ -272,7 +272,7 @@ def test_sparse_all_tokens_equals_dense_and_order_free():
 
 def test_sparse_token_subset_matches_gathered_attention():
     inp = _custom(B=1, lens=(500,), H=4)
-    pos = torch.tensor([3, 499, 17, 250, 251, 0, -1, 600], dtype=torch.int32)
+    pos = torch.tensor([3, 499, 17, 250, 251, 0, -1, 600, 500], dtype=torch.int32)
     ix = pos.view(1, 1, -1)
     out, lse = oracle.decode(inp, indices=ix)
     keep = [3, 499, 17, 250, 251, 0]

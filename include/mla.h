@@ -1,0 +1,155 @@
+/*
+ * mla.h -- C ABI of the weight-absorbed MLA decode library (libmla.so, gfx950).
+ *
+ * What the library computes.  Multi-head Latent Attention caches, per token,
+ * only a 512-dim joint latent c^KV plus a 64-dim decoupled RoPE key k^R
+ * ("MLA & DSA 推理性能优化指南" §1.1 figure; §5.1 table: d_c = 512,
+ * d_rope = 64).  At decode time W_UK is absorbed into the query, so each head
+ * scores the cached latent directly ("MLA 在极长上下文下的显存带宽突围",
+ * section "运行期矩阵吸收避免潜在张量展开"):
+ *
+ *     z_j  = softmax_scale * ( q_nope . c_j  +  q_rope . k_rope_j )
+ *     out  = sum_j softmax(z)_j * c_j          (512 dims per head)
+ *     lse  = ln sum_j exp(z_j)                 (natural log)
+ *
+ * The same latent rows serve as keys (all 576 dims) and values (the first
+ * 512), so every head of a sequence reads the same 1152 bytes per cached
+ * token ("MLA & DSA 推理性能优化指南" §4.1).  The sparse variant attends only
+ * over a given list of token positions, the DSA top-k selection of
+ * "MLA & DSA 推理性能优化指南" §1.2 and §4.2.
+ *
+ * Data layout (all tensors dense, row-major, no strides):
+ *   q_nope        bf16  [B, Sq, H, 512]
+ *   q_rope        bf16  [B, Sq, H, 64]
+ *   kv_pages      [num_pages, 64, 576]: per token the row [c (0..511) | k_rope
+ *                 (512..575)]; bf16, or one OCP e4m3fn byte per element
+ *   kv_scales     fp32  [num_pages, 64]: per-token dequant scale (fp8 only);
+ *                 a token's value is e4m3fn(code) * scale
+ *   block_table   int32 [B, bt_stride]: physical page of each 64-token logical
+ *                 page of sequence b
+ *   cache_seqlens int32 [B]: tokens in the cache of sequence b, the Sq new
+ *                 tokens included
+ *   indices       int32 [B, Sq, topk]: logical token positions (sparse only)
+ *   out           bf16  [B, Sq, H, 512]
+ *   lse           fp32  [B, Sq, H]
+ *
+ * Visibility.  Dense: token j of sequence b is visible to query s iff
+ * j < L_b and, when causal != 0, j <= L_b - Sq + s.  Sparse: the listed
+ * positions with 0 <= idx < L_b (no causal rule; entries are expected to be
+ * distinct).  In both, a token whose logical page p has p >= bt_stride or a
+ * block_table entry outside [0, num_pages) is not visible.  Cache bytes of
+ * tokens that are not visible never influence results (they may hold NaN).
+ * A query with no visible token gets out = 0 and lse = -inf.
+ *
+ * Ownership and execution.  Every pointer except those documented as host
+ * pointers is a device pointer owned by the caller.  Calls validate their
+ * arguments on the host, then only enqueue kernels on `stream`: they never
+ * allocate or free device memory and never synchronise, so they can be
+ * captured into a HIP graph.  The only library state is a per-device cache
+ * of the compute-unit count and a thread-local error string.
+ *
+ * Errors.  Every entry point returns an mla_status.  All validation happens
+ * before anything is enqueued, so a call that returns a validation error has
+ * not touched `out`, `lse` or the workspace.  MLA_ERR_HIP means a launch
+ * failed; `out`/`lse` are then undefined.  mla_last_error() gives a detail
+ * string for the calling thread's last failing call.
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  MLA_DC = 512,   /* latent (value) dims, d_c */
+  MLA_DROPE = 64, /* decoupled RoPE key dims, d_rope */
+  MLA_DLAT = 576, /* cached dims per token, d_c + d_rope */
+  MLA_PAGE = 64,  /* tokens per cache page */
+  MLA_MAX_ROWS_PER_UNIT = 128
+};
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_NULL = 1,        /* a required pointer is NULL */
+  MLA_ERR_SHAPE = 2,       /* a size or scalar argument is out of range */
+  MLA_ERR_UNSUPPORTED = 3, /* valid request this build does not handle */
+  MLA_ERR_ALIGN = 4,       /* a pointer breaks the alignment rule below */
+  MLA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required */
+  MLA_ERR_HIP = 6          /* a HIP call or kernel launch failed */
+} mla_status;
+
+typedef enum { MLA_KV_BF16 = 0, MLA_KV_FP8_E4M3 = 1 } mla_kv_dtype;
+
+/*
+ * Bytes of device workspace a call with these sizes needs (0 on invalid
+ * sizes).  topk = 0 selects the dense path, topk > 0 the sparse path.
+ * num_wg is the number of persistent workgroups the work is spread over;
+ * 0 means one per compute unit of the current device.  The same
+ * (B, Sq, H, topk, num_wg) must be passed to mla_plan / mla_decode /
+ * mla_sparse_decode with a workspace of at least this size.  The size does
+ * not depend on the cache lengths.
+ */
+size_t mla_workspace_size(int B, int Sq, int H, int topk, int num_wg);
+
+/*
+ * Split-KV scheduling pass: reads cache_seqlens on the device and writes the
+ * work partition (which workgroup processes which 64-token tiles of which
+ * sequence, and where each partial result goes) into the workspace.  It is
+ * what mla_decode / mla_sparse_decode run first when `planned` is 0.  Run it
+ * once per decode step and pass planned = 1 to every layer's call to reuse
+ * the partition (valid while cache_seqlens and the sizes stay the same).
+ * Alignment: workspace 256 B.
+ */
+mla_status mla_plan(const int32_t *cache_seqlens, int B, int Sq, int H, int topk, int num_wg,
+                    void *workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Dense absorbed MLA decode (see the definition above).
+ *   kv_dtype      MLA_KV_BF16, or MLA_KV_FP8_E4M3 with kv_scales non-NULL
+ *   num_pages     pages in kv_pages (>= 1)
+ *   bt_stride     int32 entries per block_table row (>= 1)
+ *   softmax_scale finite multiplier of the scores (e.g. 1/sqrt(192))
+ *   causal        nonzero: query s sees tokens j <= L_b - Sq + s
+ *   planned       nonzero: mla_plan already filled this workspace
+ * Limits: 1 <= Sq*H; sequences with Sq*H > 128 rows are processed as
+ * several 128-row blocks, each reading the cache once.
+ * Alignment: q_nope, q_rope, kv_pages, kv_scales, out 16 B; workspace 256 B.
+ */
+mla_status mla_decode(const void *q_nope, const void *q_rope, const void *kv_pages,
+                      const float *kv_scales, mla_kv_dtype kv_dtype, int num_pages,
+                      const int32_t *block_table, int bt_stride, const int32_t *cache_seqlens,
+                      int B, int Sq, int H, float softmax_scale, int causal, void *out,
+                      float *lse, void *workspace, size_t ws_bytes, int num_wg, int planned,
+                      hipStream_t stream);
+
+/*
+ * Sparse (DSA top-k) absorbed MLA decode: query (b, s) attends over the
+ * positions indices[b, s, 0..topk) (see "Visibility" above).  Arguments as
+ * mla_decode, plus indices and topk (>= 1); there is no causal rule.  Each
+ * (b, s) is scheduled as its own unit of H rows.
+ */
+mla_status mla_sparse_decode(const void *q_nope, const void *q_rope, const void *kv_pages,
+                             const float *kv_scales, mla_kv_dtype kv_dtype, int num_pages,
+                             const int32_t *block_table, int bt_stride,
+                             const int32_t *cache_seqlens, const int32_t *indices, int topk,
+                             int B, int Sq, int H, float softmax_scale, void *out, float *lse,
+                             void *workspace, size_t ws_bytes, int num_wg, int planned,
+                             hipStream_t stream);
+
+/* Static name of a status code ("MLA_OK", ...). */
+const char *mla_status_str(mla_status s);
+
+/* Detail message of the calling thread's last non-OK return ("" if none). */
+const char *mla_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H_ */

@@ -1,0 +1,176 @@
+"""Python binding of libmla (weight-absorbed MLA decode on gfx950).
+
+Argument marshalling only: every step of the decode runs in the HIP kernels
+behind the C ABI declared in include/mla.h.  PyTorch provides device memory
+and the current HIP stream.  There is no fallback: if libmla.so is missing
+or the tensors are not on a GPU, calls raise.
+
+    out, lse = decode(q_nope, q_rope, kv_pages, block_table, cache_seqlens,
+                      softmax_scale, kv_scales=None, causal=False)
+    out, lse = sparse_decode(q_nope, q_rope, kv_pages, block_table,
+                             cache_seqlens, indices, softmax_scale)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmla.so")
+
+MLA_KV_BF16 = 0
+MLA_KV_FP8_E4M3 = 1
+STATUS = ["MLA_OK", "MLA_ERR_NULL", "MLA_ERR_SHAPE", "MLA_ERR_UNSUPPORTED", "MLA_ERR_ALIGN",
+          "MLA_ERR_WORKSPACE", "MLA_ERR_HIP"]
+EXPORTS = ["mla_workspace_size", "mla_plan", "mla_decode", "mla_sparse_decode", "mla_status_str",
+           "mla_last_error"]
+
+_lib = None
+
+
+class MLAError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        name = STATUS[status] if 0 <= status < len(STATUS) else str(status)
+        super().__init__(f"{name}: {detail}")
+        self.status = status
+
+
+def lib():
+    """The loaded libmla.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() or "
+                              "python mla_latent_kv_12_amd/build.py")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, sz, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
+        L.mla_workspace_size.restype = sz
+        L.mla_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+        L.mla_plan.restype = i32
+        L.mla_plan.argtypes = [vp, i32, i32, i32, i32, i32, vp, sz, vp]
+        L.mla_decode.restype = i32
+        L.mla_decode.argtypes = [vp, vp, vp, vp, i32, i32, vp, i32, vp, i32, i32, i32, f32, i32,
+                                 vp, vp, vp, sz, i32, i32, vp]
+        L.mla_sparse_decode.restype = i32
+        L.mla_sparse_decode.argtypes = [vp, vp, vp, vp, i32, i32, vp, i32, vp, vp, i32, i32, i32,
+                                        i32, f32, vp, vp, vp, sz, i32, i32, vp]
+        L.mla_status_str.restype = ctypes.c_char_p
+        L.mla_status_str.argtypes = [i32]
+        L.mla_last_error.restype = ctypes.c_char_p
+        L.mla_last_error.argtypes = []
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise MLAError(status, lib().mla_last_error().decode())
+
+
+def workspace_size(B: int, Sq: int, H: int, topk: int = 0, num_wg: int = 0) -> int:
+    return int(lib().mla_workspace_size(B, Sq, H, topk, num_wg))
+
+
+def alloc_workspace(B: int, Sq: int, H: int, topk: int = 0, num_wg: int = 0, device=None):
+    n = workspace_size(B, Sq, H, topk, num_wg)
+    if n == 0:
+        raise MLAError(2, "invalid sizes for the workspace")
+    return torch.empty(n, dtype=torch.uint8, device=device or torch.device("cuda"))
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _req(t, name, dtypes, dim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU (no CPU path exists)")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dim is not None and t.dim() != dim:
+        raise ValueError(f"{name} must have {dim} dims, has {t.dim()}")
+
+
+def _common(q_nope, q_rope, kv_pages, kv_scales, block_table, cache_seqlens, out, lse, workspace,
+            topk, num_wg):
+    _req(q_nope, "q_nope", (torch.bfloat16,), 4)
+    _req(q_rope, "q_rope", (torch.bfloat16,), 4)
+    B, Sq, H, dc = q_nope.shape
+    if dc != 512 or tuple(q_rope.shape) != (B, Sq, H, 64):
+        raise ValueError("q_nope must be [B,Sq,H,512] and q_rope [B,Sq,H,64]")
+    _req(kv_pages, "kv_pages", (torch.bfloat16, torch.uint8, torch.float8_e4m3fn), 3)
+    if tuple(kv_pages.shape[1:]) != (64, 576):
+        raise ValueError("kv_pages must be [num_pages, 64, 576]")
+    fp8 = kv_pages.dtype != torch.bfloat16
+    if fp8:
+        if kv_scales is None:
+            raise ValueError("an fp8 cache needs kv_scales")
+        _req(kv_scales, "kv_scales", (torch.float32,), 2)
+        if tuple(kv_scales.shape) != (kv_pages.shape[0], 64):
+            raise ValueError("kv_scales must be [num_pages, 64]")
+    _req(block_table, "block_table", (torch.int32,), 2)
+    if block_table.shape[0] != B:
+        raise ValueError("block_table must be [B, max_pages]")
+    _req(cache_seqlens, "cache_seqlens", (torch.int32,), 1)
+    if cache_seqlens.shape[0] != B:
+        raise ValueError("cache_seqlens must be [B]")
+    dev = q_nope.device
+    if out is None:
+        out = torch.empty((B, Sq, H, 512), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((B, Sq, H), dtype=torch.float32, device=dev)
+    _req(out, "out", (torch.bfloat16,), 4)
+    _req(lse, "lse", (torch.float32,), 3)
+    if tuple(out.shape) != (B, Sq, H, 512) or tuple(lse.shape) != (B, Sq, H):
+        raise ValueError("out must be [B,Sq,H,512] and lse [B,Sq,H]")
+    if workspace is None:
+        workspace = alloc_workspace(B, Sq, H, topk, num_wg, dev)
+    _req(workspace, "workspace", (torch.uint8,), 1)
+    return B, Sq, H, fp8, out, lse, workspace
+
+
+def plan(cache_seqlens: torch.Tensor, B: int, Sq: int, H: int, workspace: torch.Tensor,
+         topk: int = 0, num_wg: int = 0):
+    """Run the split-KV scheduling pass into `workspace` (see mla_plan)."""
+    _req(cache_seqlens, "cache_seqlens", (torch.int32,), 1)
+    _req(workspace, "workspace", (torch.uint8,), 1)
+    _check(lib().mla_plan(cache_seqlens.data_ptr(), B, Sq, H, topk, num_wg, workspace.data_ptr(),
+                          workspace.numel(), _stream(cache_seqlens)))
+
+
+def decode(q_nope, q_rope, kv_pages, block_table, cache_seqlens, softmax_scale, kv_scales=None,
+           causal=False, out=None, lse=None, workspace=None, num_wg=0, planned=False):
+    """Dense absorbed MLA decode; returns (out bf16 [B,Sq,H,512], lse fp32 [B,Sq,H])."""
+    B, Sq, H, fp8, out, lse, workspace = _common(q_nope, q_rope, kv_pages, kv_scales, block_table,
+                                                 cache_seqlens, out, lse, workspace, 0, num_wg)
+    _check(lib().mla_decode(
+        q_nope.data_ptr(), q_rope.data_ptr(), kv_pages.data_ptr(),
+        kv_scales.data_ptr() if fp8 else None, MLA_KV_FP8_E4M3 if fp8 else MLA_KV_BF16,
+        kv_pages.shape[0], block_table.data_ptr(), block_table.shape[1], cache_seqlens.data_ptr(),
+        B, Sq, H, float(softmax_scale), int(bool(causal)), out.data_ptr(), lse.data_ptr(),
+        workspace.data_ptr(), workspace.numel(), int(num_wg), int(bool(planned)), _stream(q_nope)))
+    return out, lse
+
+
+def sparse_decode(q_nope, q_rope, kv_pages, block_table, cache_seqlens, indices, softmax_scale,
+                  kv_scales=None, out=None, lse=None, workspace=None, num_wg=0, planned=False):
+    """DSA top-k absorbed MLA decode over indices [B,Sq,topk]; returns (out, lse)."""
+    _req(indices, "indices", (torch.int32,), 3)
+    topk = indices.shape[2]
+    B, Sq, H, fp8, out, lse, workspace = _common(q_nope, q_rope, kv_pages, kv_scales, block_table,
+                                                 cache_seqlens, out, lse, workspace, topk, num_wg)
+    if tuple(indices.shape[:2]) != (B, Sq):
+        raise ValueError("indices must be [B, Sq, topk]")
+    _check(lib().mla_sparse_decode(
+        q_nope.data_ptr(), q_rope.data_ptr(), kv_pages.data_ptr(),
+        kv_scales.data_ptr() if fp8 else None, MLA_KV_FP8_E4M3 if fp8 else MLA_KV_BF16,
+        kv_pages.shape[0], block_table.data_ptr(), block_table.shape[1], cache_seqlens.data_ptr(),
+        indices.data_ptr(), topk, B, Sq, H, float(softmax_scale), out.data_ptr(), lse.data_ptr(),
+        workspace.data_ptr(), workspace.numel(), int(num_wg), int(bool(planned)), _stream(q_nope)))
+    return out, lse

@@ -1,0 +1,230 @@
+// C ABI of libmla: argument validation, workspace sizing and kernel launches.
+// Every check runs before anything is enqueued; launches never allocate,
+// free or synchronise.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "mla.h"
+#include "mla_internal.h"
+
+namespace {
+
+thread_local char g_err[512];
+
+mla_status fail(mla_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+mla_status fail(mla_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+// Compute-unit count per device, queried once.
+int device_cus() {
+  static std::mutex mu;
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  std::lock_guard<std::mutex> lk(mu);
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+constexpr int kMaxWg = 1 << 16;
+
+// Folds the request into scheduling units; returns false on invalid sizes.
+bool make_geometry(int B, int Sq, int H, int topk, int num_wg, mla::Geometry* g) {
+  if (B <= 0 || Sq <= 0 || H <= 0 || topk < 0 || num_wg < 0 || num_wg > kMaxWg) return false;
+  long long m_full = topk > 0 ? (long long)H : (long long)Sq * H;
+  long long n_su = topk > 0 ? (long long)B * Sq : (long long)B;
+  if (m_full > (1 << 24) || n_su > (1 << 24)) return false;
+  g->B = B;
+  g->Sq = Sq;
+  g->H = H;
+  g->sparse = topk > 0;
+  g->topk = topk;
+  g->n_su = (int)n_su;
+  g->m_full = (int)m_full;
+  g->row_blocks = (int)((m_full + mla::kMaxUnitRows - 1) / mla::kMaxUnitRows);
+  long long units = n_su * g->row_blocks;
+  if (units > (1 << 24)) return false;
+  g->n_units = (int)units;
+  g->m_unit = (int)(m_full < mla::kMaxUnitRows ? m_full : mla::kMaxUnitRows);
+  g->num_wg = num_wg;
+  g->max_splits = num_wg + g->n_units;
+  return true;
+}
+
+int resolve_wg(int num_wg) { return num_wg > 0 ? num_wg : device_cus(); }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+mla_status fill_sched_args(const mla::Geometry& g, const int32_t* seqlens, void* ws,
+                           mla::DecodeArgs* a) {
+  mla::WsLayout w = mla::ws_layout(g);
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  a->seqlens = seqlens;
+  a->ws_work = reinterpret_cast<int32_t*>(base + w.work);
+  a->ws_cost = reinterpret_cast<int32_t*>(base + w.cost);
+  a->ws_meta = reinterpret_cast<int32_t*>(base + w.meta);
+  a->ws_plse = reinterpret_cast<float*>(base + w.plse);
+  a->ws_po = reinterpret_cast<float*>(base + w.po);
+  a->B = g.B;
+  a->Sq = g.Sq;
+  a->H = g.H;
+  a->topk = g.topk;
+  a->n_su = g.n_su;
+  a->m_full = g.m_full;
+  a->row_blocks = g.row_blocks;
+  a->n_units = g.n_units;
+  a->num_wg = g.num_wg;
+  return MLA_OK;
+}
+
+mla_status run(const void* q_nope, const void* q_rope, const void* kv_pages, const float* kv_scales,
+               mla_kv_dtype kv_dtype, int num_pages, const int32_t* block_table, int bt_stride,
+               const int32_t* cache_seqlens, const int32_t* indices, int topk, int B, int Sq,
+               int H, float softmax_scale, int causal, void* out, float* lse, void* workspace,
+               size_t ws_bytes, int num_wg, int planned, hipStream_t stream) {
+  g_err[0] = 0;
+  if (!q_nope || !q_rope || !kv_pages || !block_table || !cache_seqlens || !out || !lse)
+    return fail(MLA_ERR_NULL, "a required tensor pointer is NULL");
+  if (topk > 0 && !indices) return fail(MLA_ERR_NULL, "sparse decode needs indices");
+  if (kv_dtype != MLA_KV_BF16 && kv_dtype != MLA_KV_FP8_E4M3)
+    return fail(MLA_ERR_SHAPE, "unknown kv_dtype %d", (int)kv_dtype);
+  if (kv_dtype == MLA_KV_FP8_E4M3 && !kv_scales)
+    return fail(MLA_ERR_NULL, "fp8 cache needs kv_scales");
+  if (B <= 0 || Sq <= 0 || H <= 0) return fail(MLA_ERR_SHAPE, "B, Sq, H must be >= 1 (got %d, %d, %d)", B, Sq, H);
+  if (num_pages <= 0 || bt_stride <= 0)
+    return fail(MLA_ERR_SHAPE, "num_pages and bt_stride must be >= 1 (got %d, %d)", num_pages, bt_stride);
+  if (!isfinite(softmax_scale)) return fail(MLA_ERR_SHAPE, "softmax_scale must be finite");
+  if (num_wg < 0 || num_wg > kMaxWg) return fail(MLA_ERR_SHAPE, "num_wg out of range [0, %d]", kMaxWg);
+  if (!aligned(q_nope, 16) || !aligned(q_rope, 16) || !aligned(kv_pages, 16) || !aligned(out, 16) ||
+      (kv_scales && !aligned(kv_scales, 16)) || !aligned(lse, 4) || !aligned(block_table, 4) ||
+      !aligned(cache_seqlens, 4) || (indices && !aligned(indices, 4)))
+    return fail(MLA_ERR_ALIGN, "tensor pointer misaligned (16 B for q/kv/scales/out, 4 B for the rest)");
+  if (!workspace) return fail(MLA_ERR_WORKSPACE, "workspace is NULL");
+  if (!aligned(workspace, 256)) return fail(MLA_ERR_ALIGN, "workspace must be 256-byte aligned");
+  const int wg = resolve_wg(num_wg);
+  if (wg <= 0) return fail(MLA_ERR_HIP, "could not query the device's compute units");
+  mla::Geometry g;
+  if (!make_geometry(B, Sq, H, topk, wg, &g)) return fail(MLA_ERR_SHAPE, "sizes out of range");
+  const size_t need = mla::ws_layout(g).total;
+  if (ws_bytes < need)
+    return fail(MLA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
+  if ((long long)num_pages * mla::kPage * mla::kD * (kv_dtype == MLA_KV_BF16 ? 2 : 1) < 0)
+    return fail(MLA_ERR_SHAPE, "num_pages too large");
+
+  mla::DecodeArgs a;
+  memset(&a, 0, sizeof a);
+  fill_sched_args(g, cache_seqlens, workspace, &a);
+  a.q_nope = static_cast<const uint16_t*>(q_nope);
+  a.q_rope = static_cast<const uint16_t*>(q_rope);
+  a.kv = static_cast<const uint8_t*>(kv_pages);
+  a.kv_scales = kv_scales;
+  a.block_table = block_table;
+  a.indices = indices;
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  a.bt_stride = bt_stride;
+  a.num_pages = num_pages;
+  a.causal = (topk == 0 && causal) ? 1 : 0;
+  a.scale_log2 = softmax_scale * 1.44269504088896340736f;
+
+  hipError_t e;
+  if (!planned) {
+    e = mla::launch_plan(g, a, stream);
+    if (e != hipSuccess) return fail(MLA_ERR_HIP, "plan launch: %s", hipGetErrorString(e));
+  }
+  e = mla::launch_decode(g, a, kv_dtype == MLA_KV_FP8_E4M3, stream);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+  e = mla::launch_combine(g, a, stream);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "combine launch: %s", hipGetErrorString(e));
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mla_workspace_size(int B, int Sq, int H, int topk, int num_wg) {
+  mla::Geometry g;
+  if (num_wg < 0 || num_wg > kMaxWg) return 0;
+  const int wg = resolve_wg(num_wg);
+  if (wg <= 0 || !make_geometry(B, Sq, H, topk, wg, &g)) return 0;
+  return mla::ws_layout(g).total;
+}
+
+mla_status mla_plan(const int32_t* cache_seqlens, int B, int Sq, int H, int topk, int num_wg,
+                    void* workspace, size_t ws_bytes, hipStream_t stream) {
+  g_err[0] = 0;
+  if (!cache_seqlens) return fail(MLA_ERR_NULL, "cache_seqlens is NULL");
+  if (!workspace) return fail(MLA_ERR_WORKSPACE, "workspace is NULL");
+  if (!aligned(workspace, 256)) return fail(MLA_ERR_ALIGN, "workspace must be 256-byte aligned");
+  if (!aligned(cache_seqlens, 4)) return fail(MLA_ERR_ALIGN, "cache_seqlens must be 4-byte aligned");
+  if (B <= 0 || Sq <= 0 || H <= 0 || topk < 0) return fail(MLA_ERR_SHAPE, "B, Sq, H must be >= 1 and topk >= 0");
+  if (num_wg < 0 || num_wg > kMaxWg) return fail(MLA_ERR_SHAPE, "num_wg out of range [0, %d]", kMaxWg);
+  const int wg = resolve_wg(num_wg);
+  if (wg <= 0) return fail(MLA_ERR_HIP, "could not query the device's compute units");
+  mla::Geometry g;
+  if (!make_geometry(B, Sq, H, topk, wg, &g)) return fail(MLA_ERR_SHAPE, "sizes out of range");
+  const size_t need = mla::ws_layout(g).total;
+  if (ws_bytes < need) return fail(MLA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
+  mla::DecodeArgs a;
+  memset(&a, 0, sizeof a);
+  fill_sched_args(g, cache_seqlens, workspace, &a);
+  hipError_t e = mla::launch_plan(g, a, stream);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "plan launch: %s", hipGetErrorString(e));
+  return MLA_OK;
+}
+
+mla_status mla_decode(const void* q_nope, const void* q_rope, const void* kv_pages,
+                      const float* kv_scales, mla_kv_dtype kv_dtype, int num_pages,
+                      const int32_t* block_table, int bt_stride, const int32_t* cache_seqlens,
+                      int B, int Sq, int H, float softmax_scale, int causal, void* out,
+                      float* lse, void* workspace, size_t ws_bytes, int num_wg, int planned,
+                      hipStream_t stream) {
+  return run(q_nope, q_rope, kv_pages, kv_scales, kv_dtype, num_pages, block_table, bt_stride,
+             cache_seqlens, nullptr, 0, B, Sq, H, softmax_scale, causal, out, lse, workspace,
+             ws_bytes, num_wg, planned, stream);
+}
+
+mla_status mla_sparse_decode(const void* q_nope, const void* q_rope, const void* kv_pages,
+                             const float* kv_scales, mla_kv_dtype kv_dtype, int num_pages,
+                             const int32_t* block_table, int bt_stride,
+                             const int32_t* cache_seqlens, const int32_t* indices, int topk,
+                             int B, int Sq, int H, float softmax_scale, void* out, float* lse,
+                             void* workspace, size_t ws_bytes, int num_wg, int planned,
+                             hipStream_t stream) {
+  g_err[0] = 0;
+  if (topk <= 0) return fail(MLA_ERR_SHAPE, "topk must be >= 1 (got %d)", topk);
+  return run(q_nope, q_rope, kv_pages, kv_scales, kv_dtype, num_pages, block_table, bt_stride,
+             cache_seqlens, indices, topk, B, Sq, H, softmax_scale, 0, out, lse, workspace, ws_bytes,
+             num_wg, planned, stream);
+}
+
+const char* mla_status_str(mla_status s) {
+  switch (s) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_NULL: return "MLA_ERR_NULL";
+    case MLA_ERR_SHAPE: return "MLA_ERR_SHAPE";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED";
+    case MLA_ERR_ALIGN: return "MLA_ERR_ALIGN";
+    case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP";
+  }
+  return "MLA_ERR_UNKNOWN";
+}
+
+const char* mla_last_error(void) { return g_err; }
+
+}  // extern "C"

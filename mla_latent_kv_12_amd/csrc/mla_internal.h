@@ -1,0 +1,80 @@
+// Internal declarations shared by the kernels and the C-ABI layer of libmla.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mla {
+
+constexpr int kDC = 512;             // latent dims (value part)
+constexpr int kDR = 64;              // RoPE key dims
+constexpr int kD = kDC + kDR;        // 576 cached dims per token
+constexpr int kPage = 64;            // tokens per page == tokens per tile
+constexpr int kRowsPerWave = 32;     // query rows one wave owns
+constexpr int kMaxUnitRows = 128;    // query rows per scheduling unit
+constexpr int kBytesBf16Row = kD * 2;   // 1152
+constexpr int kBytesFp8Row = kD;        // 576
+constexpr int kTileBf16 = kPage * kBytesBf16Row;  // 73728
+constexpr int kTileFp8 = kPage * kBytesFp8Row;    // 36864
+
+// Scheduling constants: a split costs this many tiles of fixed work (query
+// load + partial write/read), and a workgroup is never given less work.
+constexpr int kSplitCost = 2;
+constexpr int kMinWgCost = 6;
+
+// Problem geometry after the host has folded (B, Sq, H, sparse) into units.
+// A "sequence unit" (su) is a set of query rows that attend over the same
+// tokens: dense -> one per batch entry (Sq*H rows); sparse -> one per
+// (b, s) (H rows).  Units split a sequence unit into blocks of <= 128 rows.
+struct Geometry {
+  int B, Sq, H;
+  int sparse, topk;
+  int n_su;        // sequence units
+  int m_full;      // rows per sequence unit
+  int row_blocks;  // ceil(m_full / 128)
+  int n_units;     // n_su * row_blocks
+  int m_unit;      // min(m_full, 128): selects the kernel shape
+  int num_wg;      // persistent workgroups
+  int max_splits;  // num_wg + n_units
+};
+
+struct WsLayout {
+  size_t work;   // int32 [(num_wg + 1) * 2]   (first unit, first tile) per WG
+  size_t cost;   // int32 [n_units + 1]        prefix of per-unit cost
+  size_t meta;   // int32 [n_units * 4]        n_tiles, split_base, n_splits, g_first
+  size_t plse;   // f32   [max_splits * 128]   partial log2-sum-exp
+  size_t po;     // f32   [max_splits * 128 * 512] partial normalised outputs
+  size_t total;
+};
+
+WsLayout ws_layout(const Geometry& g);
+
+struct DecodeArgs {
+  const uint16_t* q_nope;
+  const uint16_t* q_rope;
+  const uint8_t* kv;
+  const float* kv_scales;
+  const int32_t* block_table;
+  const int32_t* seqlens;
+  const int32_t* indices;
+  uint16_t* out;
+  float* lse;
+  int32_t* ws_work;
+  int32_t* ws_cost;
+  int32_t* ws_meta;
+  float* ws_plse;
+  float* ws_po;
+  int bt_stride;
+  int num_pages;
+  int B, Sq, H, topk;
+  int n_su, m_full, row_blocks, n_units, num_wg;
+  int causal;
+  float scale_log2;  // softmax_scale * log2(e)
+};
+
+hipError_t launch_plan(const Geometry& g, const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode(const Geometry& g, const DecodeArgs& a, bool fp8, hipStream_t stream);
+hipError_t launch_combine(const Geometry& g, const DecodeArgs& a, hipStream_t stream);
+
+}  // namespace mla

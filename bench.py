@@ -1,0 +1,205 @@
+"""Benchmark of the weight-absorbed MLA decode path on one MI355X.
+
+One step = one full decode of the workload through the C ABI: the split-KV
+scheduling pass (mla_plan), the main pass (mla_attend) and the split merge
+(mla_combine), over inputs already resident in HBM.  Steps rotate over
+several copies of the latent cache so consecutive steps do not find it in
+the 256 MB last-level cache.
+
+Prints one JSON line.  `value` is algorithmic TFLOP/s of the whole step;
+`roofline` describes the main kernel (mla_attend) timed with HIP events on
+the stream it runs on; `cpu_baseline` is the CPU oracle timed on a bounded
+sample of the same workload on this host.
+
+Algorithmic work (per query row and visible token): 2*576 FLOP for the
+score and 2*512 for the output, 2176 in all; bytes: every visible cached
+token once (1152 B bf16, 576 B + 4 B scale fp8), plus q (1152 B per row),
+out (1024 B per row) and lse (4 B per row), plus sparse indices.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import mla_synth as S  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA
+FLOP_PER_ROW_TOKEN = 2 * 576 + 2 * 512
+
+
+def visible_counts(inp) -> np.ndarray:
+    """Visible tokens per (b, s) row group: [B, Sq]."""
+    B, Sq = inp["B"], inp["Sq"]
+    L = inp["cache_seqlens"].numpy().astype(np.int64)
+    if inp["indices"] is not None:
+        ix = inp["indices"].numpy()
+        return ((ix >= 0) & (ix < L[:, None, None])).sum(axis=2)
+    if inp["causal"]:
+        s = np.arange(Sq)[None, :]
+        return np.clip(L[:, None] - Sq + s + 1, 0, None)
+    return np.repeat(L[:, None], Sq, axis=1)
+
+
+def algorithmic(inp):
+    """(FLOP, bytes) of one decode of `inp`."""
+    H = inp["H"]
+    vis = visible_counts(inp)
+    flop = float(vis.sum()) * H * FLOP_PER_ROW_TOKEN
+    tok_bytes = 576 + 4 if inp["kv_dtype"] == "fp8" else 1152
+    if inp["indices"] is not None:
+        tokens = float(vis.sum())          # each (b, s) reads its own list
+    else:
+        tokens = float(inp["cache_seqlens"].clamp(min=0).sum())
+    rows = inp["B"] * inp["Sq"] * H
+    nbytes = tokens * tok_bytes + rows * (1152 + 1024 + 4)
+    if inp["indices"] is not None:
+        nbytes += inp["indices"].numel() * 4
+    return flop, nbytes
+
+
+def kernel_source_sha() -> str:
+    p = os.path.join(ROOT, "mla_latent_kv_12_amd", "csrc", "mla_kernels.hip")
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per main-kernel launch from the committed counter summary,
+    or None when there is none or the kernel source changed since."""
+    p = os.path.join(ROOT, "profiles", f"traffic_attend_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    d = json.load(open(p))
+    if d.get("kernel_sha") != kernel_source_sha():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inp, target_s: float):
+    import oracle
+    cores = min(os.cpu_count() or 1, int(os.environ.get("OMP_NUM_THREADS", "16") or 16), 16)
+    H, Sq = inp["H"], inp["Sq"]
+    vis = visible_counts(inp)                     # [B, Sq]
+    per_row_flop = np.repeat(vis.reshape(-1), H) * FLOP_PER_ROW_TOKEN
+    # calibrate on a few rows, then time a sample sized to about target_s
+    t0 = time.perf_counter()
+    oracle.decode(inp, rows=range(min(cores, per_row_flop.size)), nthreads=cores)
+    dt = time.perf_counter() - t0
+    rate = per_row_flop[:cores].sum() / max(dt, 1e-6)
+    want = rate * target_s
+    n = int(np.searchsorted(np.cumsum(per_row_flop), want)) + 1
+    n = max(cores, min(n, per_row_flop.size))
+    t0 = time.perf_counter()
+    oracle.decode(inp, rows=range(n), nthreads=cores)
+    dt = time.perf_counter() - t0
+    flop = float(per_row_flop[:n].sum())
+    return {"value": round(flop / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"first {n} of {per_row_flop.size} query rows (all their visible tokens), fp64"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="dsv3_decode", choices=list(S.CONFIGS))
+    ap.add_argument("--copies", type=int, default=3, help="cache copies rotated over steps")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path is single-GPU; sharding is described in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import mla_latent_kv_12_amd as mla
+    dev = torch.device("cuda:0")
+    cfg = S.config(args.workload)
+    inp = S.make_inputs(cfg, poison=False)
+    flop, nbytes = algorithmic(inp)
+    g = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    kvs = [g["kv_pages"]] + [g["kv_pages"].clone() for _ in range(args.copies - 1)]
+    scs = [g["kv_scales"]] * args.copies if g["kv_scales"] is None else \
+        [g["kv_scales"]] + [g["kv_scales"].clone() for _ in range(args.copies - 1)]
+    B, Sq, H = inp["B"], inp["Sq"], inp["H"]
+    topk = inp["topk"]
+    ws = mla.alloc_workspace(B, Sq, H, topk)
+    out = torch.empty((B, Sq, H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, Sq, H), dtype=torch.float32, device=dev)
+
+    def step(k, ev=None):
+        i = k % args.copies
+        mla.plan(g["cache_seqlens"], B, Sq, H, ws, topk=topk)
+        if ev is not None:
+            ev[0].record()
+        mla.attend(g["q_nope"], g["q_rope"], kvs[i], g["block_table"], g["cache_seqlens"],
+                   g["softmax_scale"], ws, kv_scales=scs[i], indices=g["indices"],
+                   causal=g["causal"], out=out, lse=lse)
+        if ev is not None:
+            ev[1].record()
+        mla.combine(g["cache_seqlens"], B, Sq, H, out, lse, ws, topk=topk)
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for k in range(args.steps):
+        step(k, evs[k])
+    t_end.record()
+    torch.cuda.synchronize()
+    ms = t_start.elapsed_time(t_end) / args.steps
+    attend_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    assert torch.isfinite(lse).all(), "non-finite lse"
+
+    tflops = flop / (ms * 1e-3) / 1e12
+    achieved_gbs = nbytes / (attend_ms * 1e-3) / 1e9
+    ai = flop / nbytes
+    bound = "hbm" if ai < MFMA_BF16_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9) else "mfma"
+    if bound == "hbm":
+        roof = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4)}
+    else:
+        a_tf = flop / (attend_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(a_tf, 2), "peak": MFMA_BF16_PEAK_TFS,
+                "unit": "TFLOP/s", "frac": round(a_tf / MFMA_BF16_PEAK_TFS, 4)}
+    roof["traffic"] = measured_traffic(args.workload)
+    roof["kernel"] = "mla_attend (decode_*_r4/r2/r1)"
+    roof["kernel_ms"] = round(attend_ms, 5)
+    roof["mfma_frac"] = round(flop / (attend_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS, 4)
+
+    res = {
+        "metric": "MLA absorbed decode TFLOPS + HBM GB/s (% roofline), B=64 H=128 L~8K",
+        "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "B": B, "Sq": Sq, "H": H,
+                   "tokens": int(inp["cache_seqlens"].sum()), "kv": inp["kv_dtype"],
+                   "topk": topk, "seed": inp["seed"], "cache_copies": args.copies},
+        "gbps_step": round(nbytes / (ms * 1e-3) / 1e9, 1),
+        "alg_bytes": nbytes, "alg_flop": flop,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -142,6 +142,34 @@ mla_status mla_sparse_decode(const void *q_nope, const void *q_rope, const void 
                              void *workspace, size_t ws_bytes, int num_wg, int planned,
                              hipStream_t stream);
 
+/*
+ * The three stages that mla_decode / mla_sparse_decode run, for callers that
+ * schedule them separately (e.g. to time or overlap them):
+ *   mla_plan     split-KV partition (above)
+ *   mla_attend   the main pass: streams every 64-token tile of every
+ *                sequence once from HBM and computes softmax attention over
+ *                it for all query rows of that sequence; writes out/lse of
+ *                sequences that one workgroup finished alone, and partial
+ *                results (normalised output and log-sum-exp per row and
+ *                split) into the workspace for the others
+ *   mla_combine  merges those partials by log-sum-exp into out/lse, and
+ *                writes out = 0, lse = -inf for rows that see no token
+ * mla_attend requires a workspace that mla_plan filled for the same sizes;
+ * mla_combine requires the mla_attend that wrote the partials.  indices ==
+ * NULL with topk == 0 selects the dense path (then causal applies); the
+ * other arguments mean what they mean for mla_decode / mla_sparse_decode.
+ */
+mla_status mla_attend(const void *q_nope, const void *q_rope, const void *kv_pages,
+                      const float *kv_scales, mla_kv_dtype kv_dtype, int num_pages,
+                      const int32_t *block_table, int bt_stride, const int32_t *cache_seqlens,
+                      const int32_t *indices, int topk, int B, int Sq, int H,
+                      float softmax_scale, int causal, void *out, float *lse, void *workspace,
+                      size_t ws_bytes, int num_wg, hipStream_t stream);
+
+mla_status mla_combine(const int32_t *cache_seqlens, int B, int Sq, int H, int topk, void *out,
+                       float *lse, void *workspace, size_t ws_bytes, int num_wg,
+                       hipStream_t stream);
+
 /* Static name of a status code ("MLA_OK", ...). */
 const char *mla_status_str(mla_status s);
 

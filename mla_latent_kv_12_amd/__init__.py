@@ -24,8 +24,8 @@ MLA_KV_BF16 = 0
 MLA_KV_FP8_E4M3 = 1
 STATUS = ["MLA_OK", "MLA_ERR_NULL", "MLA_ERR_SHAPE", "MLA_ERR_UNSUPPORTED", "MLA_ERR_ALIGN",
           "MLA_ERR_WORKSPACE", "MLA_ERR_HIP"]
-EXPORTS = ["mla_workspace_size", "mla_plan", "mla_decode", "mla_sparse_decode", "mla_status_str",
-           "mla_last_error"]
+EXPORTS = ["mla_workspace_size", "mla_plan", "mla_decode", "mla_sparse_decode", "mla_attend",
+           "mla_combine", "mla_status_str", "mla_last_error"]
 
 _lib = None
 
@@ -56,6 +56,11 @@ def lib():
         L.mla_sparse_decode.restype = i32
         L.mla_sparse_decode.argtypes = [vp, vp, vp, vp, i32, i32, vp, i32, vp, vp, i32, i32, i32,
                                         i32, f32, vp, vp, vp, sz, i32, i32, vp]
+        L.mla_attend.restype = i32
+        L.mla_attend.argtypes = [vp, vp, vp, vp, i32, i32, vp, i32, vp, vp, i32, i32, i32, i32,
+                                 f32, i32, vp, vp, vp, sz, i32, vp]
+        L.mla_combine.restype = i32
+        L.mla_combine.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, sz, i32, vp]
         L.mla_status_str.restype = ctypes.c_char_p
         L.mla_status_str.argtypes = [i32]
         L.mla_last_error.restype = ctypes.c_char_p
@@ -173,4 +178,35 @@ def sparse_decode(q_nope, q_rope, kv_pages, block_table, cache_seqlens, indices,
         kv_pages.shape[0], block_table.data_ptr(), block_table.shape[1], cache_seqlens.data_ptr(),
         indices.data_ptr(), topk, B, Sq, H, float(softmax_scale), out.data_ptr(), lse.data_ptr(),
         workspace.data_ptr(), workspace.numel(), int(num_wg), int(bool(planned)), _stream(q_nope)))
+    return out, lse
+
+
+def attend(q_nope, q_rope, kv_pages, block_table, cache_seqlens, softmax_scale, workspace,
+           kv_scales=None, indices=None, causal=False, out=None, lse=None, num_wg=0):
+    """Main pass only (mla_attend); `workspace` must hold a plan for these sizes."""
+    topk = 0
+    if indices is not None:
+        _req(indices, "indices", (torch.int32,), 3)
+        topk = indices.shape[2]
+    B, Sq, H, fp8, out, lse, workspace = _common(q_nope, q_rope, kv_pages, kv_scales, block_table,
+                                                 cache_seqlens, out, lse, workspace, topk, num_wg)
+    _check(lib().mla_attend(
+        q_nope.data_ptr(), q_rope.data_ptr(), kv_pages.data_ptr(),
+        kv_scales.data_ptr() if fp8 else None, MLA_KV_FP8_E4M3 if fp8 else MLA_KV_BF16,
+        kv_pages.shape[0], block_table.data_ptr(), block_table.shape[1], cache_seqlens.data_ptr(),
+        indices.data_ptr() if indices is not None else None, topk, B, Sq, H, float(softmax_scale),
+        int(bool(causal)), out.data_ptr(), lse.data_ptr(), workspace.data_ptr(), workspace.numel(),
+        int(num_wg), _stream(q_nope)))
+    return out, lse
+
+
+def combine(cache_seqlens, B, Sq, H, out, lse, workspace, topk=0, num_wg=0):
+    """Split merge only (mla_combine) after attend()."""
+    _req(cache_seqlens, "cache_seqlens", (torch.int32,), 1)
+    _req(out, "out", (torch.bfloat16,), 4)
+    _req(lse, "lse", (torch.float32,), 3)
+    _req(workspace, "workspace", (torch.uint8,), 1)
+    _check(lib().mla_combine(cache_seqlens.data_ptr(), B, Sq, H, topk, out.data_ptr(),
+                             lse.data_ptr(), workspace.data_ptr(), workspace.numel(), int(num_wg),
+                             _stream(out)))
     return out, lse

@@ -40,6 +40,7 @@ int device_cus() {
 }
 
 constexpr int kMaxWg = 1 << 16;
+constexpr int kStagePlan = 1, kStageAttend = 2, kStageCombine = 4;
 
 // Folds the request into scheduling units; returns false on invalid sizes.
 bool make_geometry(int B, int Sq, int H, int topk, int num_wg, mla::Geometry* g) {
@@ -94,7 +95,7 @@ mla_status run(const void* q_nope, const void* q_rope, const void* kv_pages, con
                mla_kv_dtype kv_dtype, int num_pages, const int32_t* block_table, int bt_stride,
                const int32_t* cache_seqlens, const int32_t* indices, int topk, int B, int Sq,
                int H, float softmax_scale, int causal, void* out, float* lse, void* workspace,
-               size_t ws_bytes, int num_wg, int planned, hipStream_t stream) {
+               size_t ws_bytes, int num_wg, int planned, hipStream_t stream, int stages = 7) {
   g_err[0] = 0;
   if (!q_nope || !q_rope || !kv_pages || !block_table || !cache_seqlens || !out || !lse)
     return fail(MLA_ERR_NULL, "a required tensor pointer is NULL");
@@ -141,14 +142,18 @@ mla_status run(const void* q_nope, const void* q_rope, const void* kv_pages, con
   a.scale_log2 = softmax_scale * 1.44269504088896340736f;
 
   hipError_t e;
-  if (!planned) {
+  if ((stages & kStagePlan) && !planned) {
     e = mla::launch_plan(g, a, stream);
     if (e != hipSuccess) return fail(MLA_ERR_HIP, "plan launch: %s", hipGetErrorString(e));
   }
-  e = mla::launch_decode(g, a, kv_dtype == MLA_KV_FP8_E4M3, stream);
-  if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
-  e = mla::launch_combine(g, a, stream);
-  if (e != hipSuccess) return fail(MLA_ERR_HIP, "combine launch: %s", hipGetErrorString(e));
+  if (stages & kStageAttend) {
+    e = mla::launch_decode(g, a, kv_dtype == MLA_KV_FP8_E4M3, stream);
+    if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+  }
+  if (stages & kStageCombine) {
+    e = mla::launch_combine(g, a, stream);
+    if (e != hipSuccess) return fail(MLA_ERR_HIP, "combine launch: %s", hipGetErrorString(e));
+  }
   return MLA_OK;
 }
 
@@ -210,6 +215,47 @@ mla_status mla_sparse_decode(const void* q_nope, const void* q_rope, const void*
   return run(q_nope, q_rope, kv_pages, kv_scales, kv_dtype, num_pages, block_table, bt_stride,
              cache_seqlens, indices, topk, B, Sq, H, softmax_scale, 0, out, lse, workspace, ws_bytes,
              num_wg, planned, stream);
+}
+
+mla_status mla_attend(const void* q_nope, const void* q_rope, const void* kv_pages,
+                      const float* kv_scales, mla_kv_dtype kv_dtype, int num_pages,
+                      const int32_t* block_table, int bt_stride, const int32_t* cache_seqlens,
+                      const int32_t* indices, int topk, int B, int Sq, int H,
+                      float softmax_scale, int causal, void* out, float* lse, void* workspace,
+                      size_t ws_bytes, int num_wg, hipStream_t stream) {
+  g_err[0] = 0;
+  if (topk < 0 || (topk > 0) != (indices != nullptr))
+    return fail(MLA_ERR_SHAPE, "indices and topk must be both set (sparse) or NULL and 0 (dense)");
+  return run(q_nope, q_rope, kv_pages, kv_scales, kv_dtype, num_pages, block_table, bt_stride,
+             cache_seqlens, indices, topk, B, Sq, H, softmax_scale, causal, out, lse, workspace,
+             ws_bytes, num_wg, 1, stream, kStageAttend);
+}
+
+mla_status mla_combine(const int32_t* cache_seqlens, int B, int Sq, int H, int topk, void* out,
+                       float* lse, void* workspace, size_t ws_bytes, int num_wg,
+                       hipStream_t stream) {
+  g_err[0] = 0;
+  if (!cache_seqlens || !out || !lse) return fail(MLA_ERR_NULL, "a required pointer is NULL");
+  if (!workspace) return fail(MLA_ERR_WORKSPACE, "workspace is NULL");
+  if (!aligned(workspace, 256)) return fail(MLA_ERR_ALIGN, "workspace must be 256-byte aligned");
+  if (!aligned(out, 16) || !aligned(lse, 4) || !aligned(cache_seqlens, 4))
+    return fail(MLA_ERR_ALIGN, "tensor pointer misaligned (16 B for out, 4 B for the rest)");
+  if (B <= 0 || Sq <= 0 || H <= 0 || topk < 0) return fail(MLA_ERR_SHAPE, "B, Sq, H must be >= 1 and topk >= 0");
+  if (num_wg < 0 || num_wg > kMaxWg) return fail(MLA_ERR_SHAPE, "num_wg out of range [0, %d]", kMaxWg);
+  const int wg = resolve_wg(num_wg);
+  if (wg <= 0) return fail(MLA_ERR_HIP, "could not query the device's compute units");
+  mla::Geometry g;
+  if (!make_geometry(B, Sq, H, topk, wg, &g)) return fail(MLA_ERR_SHAPE, "sizes out of range");
+  const size_t need = mla::ws_layout(g).total;
+  if (ws_bytes < need) return fail(MLA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
+  mla::DecodeArgs a;
+  memset(&a, 0, sizeof a);
+  fill_sched_args(g, cache_seqlens, workspace, &a);
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  hipError_t e = mla::launch_combine(g, a, stream);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "combine launch: %s", hipGetErrorString(e));
+  return MLA_OK;
 }
 
 const char* mla_status_str(mla_status s) {

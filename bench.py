@@ -117,7 +117,18 @@ def main():
     ap.add_argument("--copies", type=int, default=3, help="cache copies rotated over steps")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run plain 1 GiB device copies (calibrates HBM byte counters)")
     args = ap.parse_args()
+    if args.copy_probe:
+        # Known traffic: each copy reads and writes exactly 1 GiB.
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": src.numel() * 4, "copies": 3}))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the path is single-GPU; sharding is described in DESIGN.md)", file=sys.stderr)

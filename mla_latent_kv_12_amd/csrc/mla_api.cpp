@@ -79,6 +79,7 @@ mla_status fill_sched_args(const mla::Geometry& g, const int32_t* seqlens, void*
   a->ws_meta = reinterpret_cast<int32_t*>(base + w.meta);
   a->ws_plse = reinterpret_cast<float*>(base + w.plse);
   a->ws_po = reinterpret_cast<float*>(base + w.po);
+  a->ws_zero = base + w.zero;
   a->B = g.B;
   a->Sq = g.Sq;
   a->H = g.H;

@@ -45,6 +45,7 @@ struct WsLayout {
   size_t meta;   // int32 [n_units * 4]        n_tiles, split_base, n_splits, g_first
   size_t plse;   // f32   [max_splits * 128]   partial log2-sum-exp
   size_t po;     // f32   [max_splits * 128 * 512] partial normalised outputs
+  size_t zero;   // 1280 zero bytes: copy source for cache rows that are not visible
   size_t total;
 };
 
@@ -65,6 +66,7 @@ struct DecodeArgs {
   int32_t* ws_meta;
   float* ws_plse;
   float* ws_po;
+  const uint8_t* ws_zero;
   int bt_stride;
   int num_pages;
   int B, Sq, H, topk;

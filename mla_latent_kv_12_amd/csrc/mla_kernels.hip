@@ -22,6 +22,8 @@
 // on different tiles of the same unit and are merged at the end of the unit.
 #include "mla_internal.h"
 
+#include <utility>
+
 namespace mla {
 namespace kern {
 
@@ -98,6 +100,8 @@ __global__ __launch_bounds__(256) void plan_kernel(DecodeArgs a) {
   }
   const int total = part[255];
   if (tid == 0) C[U] = total;
+  // the zero row the main kernel copies in place of invisible cache rows
+  if (tid < 1280 / 16) reinterpret_cast<i32x4*>(const_cast<uint8_t*>(a.ws_zero))[tid] = i32x4{0, 0, 0, 0};
   __threadfence_block();
   __syncthreads();
 
@@ -248,6 +252,24 @@ __device__ __forceinline__ float acc_get(const f32x16& v, int i) {
   float t;
   asm("v_accvgpr_read_b32 %0, %1" : "=v"(t) : "a"(v[i]));
   return t;
+}
+// v *= s when the wave-uniform flag is nonzero.  The branch is inside the
+// assembly so the compiler sees one unconditional update of the block and
+// keeps it in place (a visible branch makes it copy the accumulators).
+__device__ __forceinline__ void acc_scale_if(f32x16& v, float s, int flag) {
+  float t;
+#define MLA_SCL(i) "v_accvgpr_read_b32 %16, %" #i "\n\tv_mul_f32 %16, %16, %17\n\tv_accvgpr_write_b32 %" #i ", %16\n\t"
+  asm volatile(
+      "s_cmp_eq_u32 %18, 0\n\t"
+      "s_cbranch_scc1 1f\n\t"
+      MLA_SCL(0) MLA_SCL(1) MLA_SCL(2) MLA_SCL(3) MLA_SCL(4) MLA_SCL(5) MLA_SCL(6) MLA_SCL(7)
+      MLA_SCL(8) MLA_SCL(9) MLA_SCL(10) MLA_SCL(11) MLA_SCL(12) MLA_SCL(13) MLA_SCL(14) MLA_SCL(15)
+      "1:"
+      : "+a"(v[0]), "+a"(v[1]), "+a"(v[2]), "+a"(v[3]), "+a"(v[4]), "+a"(v[5]), "+a"(v[6]),
+        "+a"(v[7]), "+a"(v[8]), "+a"(v[9]), "+a"(v[10]), "+a"(v[11]), "+a"(v[12]), "+a"(v[13]),
+        "+a"(v[14]), "+a"(v[15]), "=&v"(t)
+      : "v"(s), "s"(flag));
+#undef MLA_SCL
 }
 
 // Workgroup i is dispatched to XCD i % 8; give each XCD a contiguous range
@@ -699,23 +721,776 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Direct HBM -> LDS copies, written as inline assembly: the kernel counts
+// them itself (s_waitcnt vmcnt with the exact number of younger copies), so
+// the compiler must neither wait for them on its own nor move them across
+// the explicit waits.  Each copy points M0 at the LDS destination (every
+// active lane writes M0 + 4*lane words of its size) and restores M0.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>(p);
+}
+// 16 bytes per lane from a wave-uniform base plus a per-lane byte offset.
+__device__ __forceinline__ void copy16_s(const void* base, uint32_t voff, uint32_t lds) {
+  uint32_t keep;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(keep)
+      : "v"(voff), "s"(base), "s"(lds));
+}
+// 16 bytes per lane from a per-lane address.
+__device__ __forceinline__ void copy16_v(const void* addr, uint32_t lds) {
+  uint32_t keep;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(keep)
+      : "v"(addr), "s"(lds));
+}
+// 4 bytes per lane from a per-lane address.
+__device__ __forceinline__ void copy4_v(const void* addr, uint32_t lds) {
+  uint32_t keep;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(keep)
+      : "v"(addr), "s"(lds));
+}
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Score-operand LDS reads issued from assembly with explicit counted waits:
+// left to itself the compiler keeps only one or two of them in flight, and
+// each MFMA then waits out a full LDS round trip.
+template <int OFF>
+__device__ __forceinline__ void lds_rd16(bf16x8& dst, uint32_t addr) {
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(dst) : "v"(addr), "n"(OFF));
+}
+template <int OFF>
+__device__ __forceinline__ void lds_rd8(u32x2& dst, uint32_t addr) {
+  asm volatile("ds_read_b64 %0, %1 offset:%2" : "=v"(dst) : "v"(addr), "n"(OFF));
+}
+// Wait until at most N LDS operations are outstanding; `v` (the register
+// the caller is about to use) is tied to the wait so its use cannot move
+// above it.
+template <int N, typename V>
+__device__ __forceinline__ void lds_ready(V& v) {
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(v) : "n"(N));
+}
+template <typename F, int... I>
+__device__ __forceinline__ void unroll_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+// f(std::integral_constant<int, i>) for i = 0 .. N-1, in order.
+template <int N, typename F>
+__device__ __forceinline__ void unroll(F&& f) {
+  unroll_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// bf16 region-A swizzle of a cached row: the 16-byte chunk c of row r sits at
+// position c ^ sw16(r).  The score operand reads one chunk of 16 consecutive
+// rows per 16 lanes (sw16 is a bijection on r & 15) and the transposed value
+// reads take 4 chunks of 4 consecutive rows per 32 lanes; both cover every
+// bank once.
+__device__ __forceinline__ int sw16(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+
+// ---------------------------------------------------------------------------
+// Main kernel for units of 33..128 query rows ("wide" units).
+//
+// The R waves of a workgroup work on the same 32-token chunk of the cache
+// (half a page).  For the scores each wave owns 32 query rows (its Q stays
+// in registers); for P.V each wave owns 512/R output dims of all rows, with
+// P passed between the waves through LDS, so each chunk's values are read
+// out of LDS (transposed) once.
+//
+// Pipeline.  The workgroup walks its chunks ("items") in order, over all
+// the units its share of the work touches.  At step s it computes item s,
+// copies item s+3 from HBM into LDS (those copies are spread between the
+// score MFMAs of item s), and looks up what item s+6 needs: its page
+// (dense), or its 32 page numbers (sparse; the 32 token positions of item
+// s+9 are fetched at the same time).  Every lookup lands in LDS through the
+// same direct copies, so nothing in the loop waits on a scalar load and
+// three chunks (108 KB bf16) are in flight per compute unit.
+//
+// Item descriptors (LDS ring, 8 ints): unit (-1 past the end of the
+// workgroup's work), 2*tile + half (-1: no chunk), page (dense) or sequence
+// (sparse), sequence length, mask of visible tokens (sparse).
+// ---------------------------------------------------------------------------
+template <bool FP8, bool SPARSE, int R>
+struct Wide {
+  static constexpr int kThreads = 64 * R;
+  static constexpr int kEB = FP8 ? 1 : 2;
+  static constexpr int kRowBytes = kD * kEB;        // 1152 | 576 per cached token
+  static constexpr int kABytes = kDC * kEB;         // 1024 | 512: latent part of a row
+  static constexpr int kRows = 32;                  // tokens per chunk
+  static constexpr int kRegB = kRows * kABytes;     // region B (RoPE part) offset
+  static constexpr int kScaleOff = kRegB + kRows * kDR * kEB;
+  static constexpr int kSlotBytes = kScaleOff + (FP8 ? 128 : 0);
+  static constexpr int kSlots = 4;
+  static constexpr int kNA = FP8 ? 16 : 32;         // 1 KB copies of region A
+  static constexpr int kNB = FP8 ? 2 : 4;           // 1 KB copies of region B
+  static constexpr int kNCopy = kNA + kNB + (FP8 ? 1 : 0);  // (+ the 32 scales)
+  // every wave issues the same number of copies per item (padded with
+  // 4-byte dummy copies), so one wait count serves all of them
+  static constexpr int kPerWave = (kNCopy + R - 1) / R;
+  static_assert(kNA % R == 0, "region-A copies must split evenly over the waves");
+  static constexpr int kLook = SPARSE ? 2 : 1;      // lookup copies per step (wave 0)
+  static constexpr int kLeadDma = kSlots - 1;
+  static constexpr int kLeadPage = 2 * kLeadDma;
+  static constexpr int kLeadCur = SPARSE ? 3 * kLeadDma : kLeadPage;
+  static constexpr int kRing = SPARSE ? 16 : 8;
+  static_assert(kRing > kLeadCur, "descriptor ring too short");
+  static constexpr int kDescOff = kSlots * kSlotBytes;
+  static constexpr int kIdxOff = kDescOff + kRing * 32;
+  static constexpr int kPgOff = kIdxOff + (SPARSE ? kRing * 128 : 0);
+  static constexpr int kPOff = kPgOff + (SPARSE ? kRing * 128 : 0);
+  static constexpr int kAlphaOff = kPOff + 32 * R * 64;
+  static constexpr int kFlagOff = kAlphaOff + 32 * R * 4;
+  static constexpr int kMrgOff = kFlagOff + 16;
+  static constexpr int kDummyOff = kMrgOff + 2 * 32 * R * 4;
+  static constexpr int kLdsBytes = kDummyOff + 64;
+  static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+  static_assert(kSlotBytes % 16 == 0, "slot alignment");
+  // vector-memory operations wave w issues per step: its copies, plus the
+  // lookups of wave 0
+  static constexpr int per_step(int w) { return kPerWave + (w == 0 ? kLook : 0); }
+};
+
+template <bool FP8, bool SPARSE, int R>
+__device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
+  using W = Wide<FP8, SPARSE, R>;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int rg = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5, l32 = lane & 31;
+  const int wg = xcd_logical(blockIdx.x, gridDim.x);
+
+  uint8_t* const slots = lds;
+  int* const desc_ring = reinterpret_cast<int*>(lds + W::kDescOff);
+  int* const idx_ring = reinterpret_cast<int*>(lds + W::kIdxOff);
+  int* const pg_ring = reinterpret_cast<int*>(lds + W::kPgOff);
+  uint8_t* const pbuf = lds + W::kPOff;
+  float* const alpha_buf = reinterpret_cast<float*>(lds + W::kAlphaOff);
+  int* const flag_buf = reinterpret_cast<int*>(lds + W::kFlagOff);
+  float* const mrg = reinterpret_cast<float*>(lds + W::kMrgOff);
+  int* const dummy = reinterpret_cast<int*>(lds + W::kDummyOff);
+  auto desc = [&](int x) -> int* { return desc_ring + (x & (W::kRing - 1)) * 8; };
+  struct Desc {
+    int u, th, p2, L;  // unit, 2*tile+half, page | sequence, length
+  };
+  auto read_desc = [&](int x) -> Desc {
+    const i32x4 v = *reinterpret_cast<const i32x4*>(desc(x));
+    return Desc{__builtin_amdgcn_readfirstlane(v[0]), __builtin_amdgcn_readfirstlane(v[1]),
+                __builtin_amdgcn_readfirstlane(v[2]), __builtin_amdgcn_readfirstlane(v[3])};
+  };
+
+  // ------------------------------------------------------------ cursor
+  // The lookup cursor walks the workgroup's chunks: unit cu (-1 once done),
+  // tile ct, half ch, tile range end chi, sequence (dense b / sparse su) cs
+  // and its length cL.  Every wave runs it (uniform scalar code).
+  const int u_end = a.ws_work[2 * wg + 2], t_end = a.ws_work[2 * wg + 3];
+  int cu = a.ws_work[2 * wg], ct = a.ws_work[2 * wg + 1], ch = 0, chi = 0, cs = 0, cL = 0;
+  auto enter = [&]() {  // settle (cu, ct) on the next unit with a chunk left
+    for (;;) {
+      if (cu > u_end || cu >= a.n_units) {
+        cu = -1;
+        return;
+      }
+      chi = (cu == u_end) ? t_end : a.ws_meta[4 * cu];
+      if (ct < chi) break;
+      cu++;
+      ct = 0;
+    }
+    ch = 0;
+    cs = cu / a.row_blocks;
+    const int b = SPARSE ? cs / a.Sq : cs;
+    cL = max(a.seqlens[b], 0);
+  };
+  auto next = [&]() {
+    if (cu < 0) return;
+    const int span = SPARSE ? a.topk : cL;   // entries (tokens) of the unit
+    if (ch == 0 && kPage * ct + 32 < span) {
+      ch = 1;
+      return;
+    }
+    ct++;
+    if (ct >= chi) {
+      cu++;
+      ct = 0;
+      enter();
+    } else {
+      ch = 0;
+    }
+  };
+  enter();
+  if (cu < 0) return;  // uniform: this workgroup has no work
+
+  // Writes the descriptor of the cursor's item x and starts its lookups
+  // (wave 0): the page (dense) or the 32 token positions (sparse).  Always
+  // exactly W::kLook - (SPARSE ? 1 : 0) copies, so the counts stay exact.
+  auto lookup = [&](int x) {
+    if (rg != 0) return;
+    int* d = desc(x);
+    const int th = cu >= 0 ? 2 * ct + ch : -1;
+    if constexpr (!SPARSE) {
+      const bool need = cu >= 0 && ct < a.bt_stride;
+      if (lane == 0) {
+        d[0] = cu;
+        d[1] = th;
+        d[3] = cL;
+        if (!need) d[2] = -1;
+        const int32_t* src = need ? a.block_table + (size_t)cs * a.bt_stride + ct : a.seqlens;
+        copy4_v(src, lds_addr(need ? d + 2 : dummy));
+      }
+    } else {
+      const int b = cs / a.Sq;
+      if (lane == 0) {
+        d[0] = cu;
+        d[1] = th;
+        d[2] = b;
+        d[3] = cL;
+      }
+      const int e = kPage * ct + 32 * ch + lane;
+      const bool ok = cu >= 0 && lane < 32 && e < a.topk;
+      const bool any = __builtin_amdgcn_ballot_w64(ok) != 0;
+      int* ring = idx_ring + (x & (W::kRing - 1)) * 32;
+      if (lane < 32 && !ok) ring[lane] = -1;
+      if (any ? ok : lane == 0)
+        copy4_v(any ? a.indices + (size_t)cs * a.topk + e : a.seqlens, lds_addr(any ? ring : dummy));
+    }
+  };
+  // Sparse: start the block-table lookups of item y's 32 positions.
+  auto page_lookup = [&](int y) {
+    if constexpr (SPARSE) {
+      if (rg != 0) return;
+      const int* d = desc(y);
+      const int uu = __builtin_amdgcn_readfirstlane(d[0]);
+      const int th = __builtin_amdgcn_readfirstlane(d[1]);
+      const int bb = __builtin_amdgcn_readfirstlane(d[2]);
+      const int LL = __builtin_amdgcn_readfirstlane(d[3]);
+      const int ri = y & (W::kRing - 1);
+      const int idx = lane < 32 ? idx_ring[ri * 32 + lane] : -1;
+      const bool ok = uu >= 0 && th >= 0 && idx >= 0 && idx < LL && (idx >> 6) < a.bt_stride;
+      const bool any = __builtin_amdgcn_ballot_w64(ok) != 0;
+      if (any ? ok : lane == 0)
+        copy4_v(any ? a.block_table + (size_t)bb * a.bt_stride + (idx >> 6) : a.seqlens,
+                lds_addr(any ? pg_ring + ri * 32 : dummy));
+    }
+  };
+
+  // ------------------------------------------------------------ copies
+  struct Src {
+    const uint8_t* base;  // dense: first row of the chunk in HBM
+    const float* scales;  // dense fp8: first scale of the chunk
+    int nvalid;           // dense: visible rows at the start of the chunk
+    int tok;              // sparse: token (page*64 + row) of row `lane` (< 32), or -1
+  };
+  // Where item z's rows come from (read from its descriptor and rings).
+  auto source = [&](int z, const Desc& dz) -> Src {
+    Src r{a.ws_zero, reinterpret_cast<const float*>(a.ws_zero), 0, -1};
+    const int uu = dz.u, th = dz.th, p2 = dz.p2, LL = dz.L;
+    if constexpr (!SPARSE) {
+      if (uu >= 0 && th >= 0 && p2 >= 0 && p2 < a.num_pages) {
+        r.nvalid = min(max(LL - 32 * th, 0), 32);
+        r.base = a.kv + (size_t)p2 * (kPage * W::kRowBytes) + (th & 1) * 32 * W::kRowBytes;
+        r.scales = a.kv_scales + (size_t)p2 * kPage + (th & 1) * 32;
+      }
+    } else {
+      const int ri = z & (W::kRing - 1);
+      const int idx = lane < 32 ? idx_ring[ri * 32 + lane] : -1;
+      const int pg = lane < 32 ? pg_ring[ri * 32 + lane] : -1;
+      const bool ok = uu >= 0 && th >= 0 && idx >= 0 && idx < LL && (idx >> 6) < a.bt_stride &&
+                      pg >= 0 && pg < a.num_pages;
+      r.tok = ok ? pg * kPage + (idx & 63) : -1;
+      const unsigned m = (unsigned)__builtin_amdgcn_ballot_w64(ok);
+      if (rg == 0 && lane == 0) desc(z)[4] = (int)m;
+    }
+    return r;
+  };
+  // This wave's j-th copy of an item into the slot at LDS address `slot`.
+  // Copy i = j*R + rg of an item: region-A copies first, then region B, the
+  // fp8 scales, and padding.
+  auto copy = [&](int j, uint32_t slot, const Src& sr) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));  // keeps per-lane offsets from being hoisted out of the loop
+    const uint8_t* zero = a.ws_zero;
+    auto rowsrc = [&](int row, uint32_t off) -> const uint8_t* {  // per-lane row
+      if constexpr (!SPARSE) return row < sr.nvalid ? sr.base + row * W::kRowBytes + off : zero + off;
+      else {
+        const int t = __shfl(sr.tok, row);
+        return t >= 0 ? a.kv + (size_t)t * W::kRowBytes + off : zero + off;
+      }
+    };
+    const int i = j * R + rg;
+    if (j < W::kNA / R) {
+      if constexpr (!FP8) {  // row i, lane = 16-byte chunk position
+        const uint8_t* src;
+        if constexpr (!SPARSE) {
+          src = i < sr.nvalid ? sr.base + i * W::kRowBytes : zero;
+        } else {
+          const int t = __builtin_amdgcn_readlane(sr.tok, i);
+          src = t >= 0 ? a.kv + (size_t)t * W::kRowBytes : zero;
+        }
+        copy16_s(src, (uint32_t)((ln ^ sw16(i)) << 4), slot + i * 1024);
+      } else {  // rows 2i and 2i+1, 32 lanes each
+        const int row = 2 * i + (ln >> 5);
+        copy16_v(rowsrc(row, (uint32_t)(((ln & 31) ^ (row & 7)) << 4)), slot + i * 1024);
+      }
+      return;
+    }
+    auto region_b = [&]() {  // RoPE parts: 8 (bf16) or 16 (fp8) rows per copy
+      const int jb = i - W::kNA;
+      const int row = FP8 ? 16 * jb + (ln >> 2) : 8 * jb + (ln >> 3);
+      const int c = FP8 ? ((ln & 3) ^ (row & 3)) : ((ln & 7) ^ ((row >> 1) & 7));
+      copy16_v(rowsrc(row, (uint32_t)(W::kABytes + (c << 4))), slot + W::kRegB + jb * 1024);
+    };
+    if constexpr (!FP8 && W::kNCopy % R == 0) {
+      region_b();
+    } else {
+      if (i < W::kNA + W::kNB) {
+        region_b();
+      } else if (FP8 && i == W::kNA + W::kNB) {  // lane r < 32 copies the scale of row r
+        if (ln < 32) {
+          const float* src;
+          if constexpr (!SPARSE) src = ln < sr.nvalid ? sr.scales + ln : reinterpret_cast<const float*>(zero);
+          else src = sr.tok >= 0 ? a.kv_scales + sr.tok : reinterpret_cast<const float*>(zero);
+          copy4_v(src, slot + W::kScaleOff);
+        }
+      } else if (ln == 0) {
+        copy4_v(zero, lds_addr(dummy));
+      }
+    }
+  };
+  auto copy_all = [&](int z) {
+    const Src sr = source(z, read_desc(z));
+    const uint32_t slot = lds_addr(slots + (z % W::kSlots) * W::kSlotBytes);
+#pragma unroll
+    for (int j = 0; j < W::kPerWave; j++) copy(j, slot, sr);
+  };
+  // Wait until this wave's copies of the item about to be computed (and
+  // everything it issued before them) have landed: exactly
+  // (kLeadDma - 1) steps of younger operations may stay in flight.
+  auto wait_item = [&]() {
+    if (rg == 0) wait_vm<(W::kLeadDma - 1) * W::per_step(0)>();
+    else wait_vm<(W::kLeadDma - 1) * W::per_step(1)>();
+  };
+  // The prologue's copies are preceded by as many dummy lookups as a step
+  // makes, so the per-step count holds from the first step on.
+  auto dummy_lookups = [&]() {
+    if (rg == 0 && lane == 0) {
+#pragma unroll
+      for (int k = 0; k < W::kLook; k++) copy4_v(a.seqlens, lds_addr(dummy));
+    }
+  };
+
+  // ------------------------------------------------------------ state
+  bf16x8 qf[36];
+  f32x16 o[16];
+  float m_run = kNegInf, l_run = 0.f;
+  constexpr int DB = 16 / R;  // output dim blocks per wave
+  // o[dbl * R + rb]: O^T for dims 32*(DB*rg + dbl) .., rows 32*rb + l32.
+
+  auto load_q = [&](const UnitInfo& ui) {
+    const int r = rg * kRowsPerWave + l32;
+    const bool ok = r < ui.rows;
+    const size_t grow = (size_t)ui.row0 + (ok ? r : 0);
+    const bf16x8* qn = reinterpret_cast<const bf16x8*>(a.q_nope + grow * kDC + 8 * g);
+    const bf16x8* qr = reinterpret_cast<const bf16x8*>(a.q_rope + grow * kDR + 8 * g);
+#pragma unroll
+    for (int ks = 0; ks < 32; ks++) qf[ks] = qn[2 * ks];
+#pragma unroll
+    for (int ks = 0; ks < 4; ks++) qf[32 + ks] = qr[2 * ks];
+    if (!ok) {
+#pragma unroll
+      for (int ks = 0; ks < 36; ks++) qf[ks] = bf16x8{};
+    }
+  };
+  // Takes delivery of Q before the loop: otherwise the compiler keeps
+  // waiting for these loads inside the loop, where its count cannot see the
+  // copies (and would wait for all of them).
+  auto take_q = [&]() {
+#pragma unroll
+    for (int ks = 0; ks < 36; ks++) asm volatile("" : "+v"(qf[ks]));
+  };
+  auto reset = [&]() {
+#pragma unroll
+    for (int i = 0; i < 16; i++) o[i] = f32x16{};
+    m_run = kNegInf;
+    l_run = 0.f;
+  };
+
+  // Per-lane pieces of the swizzled LDS addresses.
+  const int G16 = lane >> 4, i16 = lane & 15;
+  const int ya = g ^ (FP8 ? 0 : sw16(l32));  // bf16 region A (score operand)
+  const int yb = g ^ ((l32 >> 1) & 7);       // bf16 region B
+  int vbase = 0, vy0 = 0, vy1 = 0;
+  int voff8[4] = {0, 0, 0, 0};
+  if constexpr (!FP8) {
+    // transposed reads: lane loads token 16ks + 8r + 4(G16>>1) + (i16>>2),
+    // dims 32db + 16(G16&1) + 4(i16&3) .. +3
+    vbase = (4 * (G16 >> 1) + (i16 >> 2)) * 1024 + 8 * (i16 & 1);
+    const int w = 2 * (G16 & 1) + ((i16 >> 1) & 1);
+    vy0 = w ^ (((i16 >> 2) << 2) | ((G16 >> 1) & 3));
+    vy1 = w ^ (((i16 >> 2) << 2) | ((2 + (G16 >> 1)) & 3));
+  } else {
+    // fp8: lane loads token 16ks + 8(i16>>3) + z8, bytes 32db + 16(G16&1) + 8(i16&1) .. +7
+    const int z8 = 4 * (G16 >> 1) + ((i16 >> 1) & 3);
+    const int trow = 8 * (i16 >> 3) + z8;
+#pragma unroll
+    for (int p4 = 0; p4 < 4; p4++) voff8[p4] = trow * 512 + (((2 * p4 + (G16 & 1)) ^ z8) << 4) + 8 * (i16 & 1);
+  }
+
+  // ------------------------------------------------------------ one step
+  // Computes item s (in `cur`) and issues this wave's copies of item z into
+  // `nxt` between the score MFMAs.
+  auto step = [&](const uint8_t* __restrict__ cur, uint32_t nxt, const Src& sr, int s,
+                  const Desc& dc, const UnitInfo& ui) {
+    const int th = dc.th;
+    int lim = 0;
+    unsigned vm = 0;
+    if constexpr (!SPARSE) {
+      const int p2 = dc.p2;
+      const int LL = dc.L;
+      const int nvalid = (th >= 0 && p2 >= 0 && p2 < a.num_pages) ? min(max(LL - 32 * th, 0), 32) : 0;
+      lim = nvalid;
+      if (a.causal) {
+        const int srow = (ui.rin_b0 + rg * kRowsPerWave + l32) / a.H;
+        lim = min(lim, LL - a.Sq + srow + 1 - 32 * th);
+      }
+    } else {
+      vm = (unsigned)__builtin_amdgcn_readfirstlane(desc(s)[4]) >> (4 * g);
+    }
+    // A chunk with nothing visible is computed like any other: its rows
+    // are zero in LDS and every weight comes out 0.
+    constexpr int kEvery = 36 / W::kPerWave;  // MFMAs between two copies
+
+    // ---- S^T[token][row] = K . Q^T over 576 dims, tokens l32 of the chunk.
+    // K operands stream through a ring of kRing registers with kLead reads
+    // in flight; a register is refilled two MFMAs after its last use.
+    f32x16 sacc = {};
+    constexpr int kLead = 6, kRingK = 8;
+    const uint32_t cur_a = lds_addr(cur);
+    wait_lds();  // nothing else outstanding: the counts below are exact
+    if constexpr (!FP8) {
+      uint32_t adA[8], adB[4];
+#pragma unroll
+      for (int k = 0; k < 8; k++) adA[k] = cur_a + l32 * 1024 + (((2 * k) ^ ya) << 4);
+#pragma unroll
+      for (int k = 0; k < 4; k++) adB[k] = cur_a + W::kRegB + l32 * 128 + (((2 * k) ^ yb) << 4);
+      bf16x8 ring[kRingK];
+      auto rd = [&](auto KS) {
+        constexpr int ks = decltype(KS)::value;
+        if constexpr (ks < 32) lds_rd16<256 * (ks >> 3)>(ring[ks % kRingK], adA[ks & 7]);
+        else lds_rd16<0>(ring[ks % kRingK], adB[ks - 32]);
+      };
+      unroll<kLead>(rd);
+      unroll<36>([&](auto KS) {
+        constexpr int ks = decltype(KS)::value;
+        lds_ready<(kLead - 1 < 35 - ks ? kLead - 1 : 35 - ks)>(ring[ks % kRingK]);
+        if constexpr (ks % kEvery == 0 && ks / kEvery < W::kPerWave) copy(ks / kEvery, nxt, sr);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[ks % kRingK], qf[ks], sacc, 0, 0, 0);
+        if constexpr (ks + kLead < 36) rd(std::integral_constant<int, ks + kLead>{});
+      });
+    } else {
+      uint32_t adA[8], adB[4];
+#pragma unroll
+      for (int k = 0; k < 8; k++) adA[k] = cur_a + l32 * 512 + 8 * g + ((k ^ (l32 & 7)) << 4);
+#pragma unroll
+      for (int k = 0; k < 4; k++) adB[k] = cur_a + W::kRegB + l32 * 64 + 8 * g + ((k ^ (l32 & 3)) << 4);
+      u32x2 ring[kRingK];
+      auto rd = [&](auto KS) {
+        constexpr int ks = decltype(KS)::value;
+        if constexpr (ks < 32) lds_rd8<128 * (ks >> 3)>(ring[ks % kRingK], adA[ks & 7]);
+        else lds_rd8<0>(ring[ks % kRingK], adB[ks - 32]);
+      };
+      unroll<kLead>(rd);
+      unroll<36>([&](auto KS) {
+        constexpr int ks = decltype(KS)::value;
+        lds_ready<(kLead - 1 < 35 - ks ? kLead - 1 : 35 - ks)>(ring[ks % kRingK]);
+        if constexpr (ks % kEvery == 0 && ks / kEvery < W::kPerWave) copy(ks / kEvery, nxt, sr);
+        const bf16x8 kf = cvt8_fp8(ring[ks % kRingK]);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc, 0, 0, 0);
+        if constexpr (ks + kLead < 36) rd(std::integral_constant<int, ks + kLead>{});
+      });
+    }
+
+    // ---- online softmax: lane holds row l32, tokens 8*(i/4) + 4g + i%4.
+    // fp8: token scales multiply the scores and, before P.V, the weights.
+    const float* scl = reinterpret_cast<const float*>(cur + W::kScaleOff) + 4 * g;
+    float mloc = kNegInf;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; q4++) {
+      f32x4 sv = {1.f, 1.f, 1.f, 1.f};
+      if constexpr (FP8) sv = *reinterpret_cast<const f32x4*>(scl + 8 * q4);
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const int i = 4 * q4 + e;
+        const int tau_rel = 8 * q4 + e;  // token minus 4g
+        float v = sacc[i] * a.scale_log2;
+        bool ok;
+        if constexpr (!SPARSE) ok = tau_rel + 4 * g < lim;
+        else ok = (vm >> tau_rel) & 1u;
+        if constexpr (FP8) v *= ok ? sv[e] : 0.f;
+        sacc[i] = ok ? v : kNegInf;
+        mloc = fmaxf(mloc, sacc[i]);
+      }
+    }
+    const float mt = pair_max(mloc);
+    const float mnew = fmaxf(m_run, mt);
+    const bool need = mnew > m_run + kRescaleSlack;  // -inf + slack = -inf
+    const bool moved = __builtin_amdgcn_ballot_w64(need) != 0;
+    // O rows only need scaling if they hold something (m was finite)
+    const bool scale_o = __builtin_amdgcn_ballot_w64(need && m_run != kNegInf) != 0;
+    float alpha = 1.f;
+    if (moved) {
+      alpha = (m_run == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m_run - mnew);
+      l_run *= alpha;
+      m_run = mnew;
+    }
+    const float muse = (m_run == kNegInf) ? 0.f : m_run;
+    float psum = 0.f;
+    bf16x8 pf[2];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; q4++) {
+      f32x4 sv = {1.f, 1.f, 1.f, 1.f};
+      if constexpr (FP8) sv = *reinterpret_cast<const f32x4*>(scl + 8 * q4);
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const int i = 4 * q4 + e;
+        float p = __builtin_amdgcn_exp2f(sacc[i] - muse);
+        psum += p;
+        if constexpr (FP8) p *= (sacc[i] == kNegInf) ? 0.f : sv[e];
+        pf[i >> 3][i & 7] = (__bf16)p;
+      }
+    }
+    l_run += psum;
+
+    // ---- P (bf16) and the rescale factors of this wave's rows go through
+    // LDS: row r, 16-byte chunk (g, kk) at position (2g + kk) ^ ((r >> 2) & 3).
+    const int pc = (l32 >> 2) & 3;
+    uint8_t* prow = pbuf + (32 * rg + l32) * 64;
+    *reinterpret_cast<bf16x8*>(prow + (((2 * g) ^ pc) << 4)) = pf[0];
+    *reinterpret_cast<bf16x8*>(prow + (((2 * g + 1) ^ pc) << 4)) = pf[1];
+    if (g == 0) alpha_buf[32 * rg + l32] = alpha;
+    if (lane == 0) flag_buf[rg] = scale_o ? 1 : 0;
+    wait_lds();
+    barrier();
+    int fl[R];
+    float al[R];
+#pragma unroll
+    for (int rb = 0; rb < R; rb++) {
+      fl[rb] = flag_buf[rb];
+      al[rb] = alpha_buf[32 * rb + l32];
+    }
+    int fany = 0;
+#pragma unroll
+    for (int rb = 0; rb < R; rb++) fany |= fl[rb];
+    if (__builtin_amdgcn_readfirstlane(fany)) {  // rare: some row's maximum moved
+#pragma unroll
+      for (int rb = 0; rb < R; rb++) {
+        const float f = __builtin_amdgcn_readfirstlane(fl[rb]) ? al[rb] : 1.f;
+#pragma unroll
+        for (int dbl = 0; dbl < DB; dbl++) acc_scale(o[dbl * R + rb], f);
+      }
+    }
+
+    // ---- O^T[dim][row] += V^T[dim][token] . P^T[token][row]; k-step kk
+    // covers tokens 16kk..16kk+15 in the accumulator order of S^T.
+    auto vload = [&](int kk, int db) -> bf16x8 {
+      if constexpr (!FP8) {
+        const uint8_t* p0 = cur + vbase + (16 * kk) * 1024 + 256 * (db >> 2) + (((4 * (db & 3)) ^ vy0) << 4);
+        const uint8_t* p1 = cur + vbase + (16 * kk + 8) * 1024 + 256 * (db >> 2) + (((4 * (db & 3)) ^ vy1) << 4);
+        const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(p0));
+        const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(p1));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+      } else {
+        const uint8_t* p = cur + voff8[db & 3] + (16 * kk) * 512 + (db >> 2) * 128;
+        return cvt8_fp8(__builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS i32x2*)(p))));
+      }
+    };
+#pragma unroll
+    for (int kk = 0; kk < 2; kk++) {
+      bf16x8 pb[R], vv[DB];
+#pragma unroll
+      for (int rb = 0; rb < R; rb++)
+        pb[rb] = *reinterpret_cast<const bf16x8*>(pbuf + (32 * rb + l32) * 64 + (((2 * g + kk) ^ pc) << 4));
+#pragma unroll
+      for (int dbl = 0; dbl < DB; dbl++) vv[dbl] = vload(kk, DB * rg + dbl);
+#pragma unroll
+      for (int dbl = 0; dbl < DB; dbl++)
+#pragma unroll
+        for (int rb = 0; rb < R; rb++)
+          o[dbl * R + rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv[dbl], pb[rb], o[dbl * R + rb], 0, 0, 0);
+    }
+  };
+
+  // ------------------------------------------------------------ epilogue
+  // Normalises this wave's dims of every row and writes them to out/lse
+  // (unit finished here) or to the unit's split partials.
+  auto end_segment = [&](const UnitInfo& ui, int uu) {
+    const float lt = pair_sum(l_run);
+    float* mm = mrg;
+    float* ll = mrg + 32 * R;
+    if (g == 0) {
+      mm[32 * rg + l32] = m_run;
+      ll[32 * rg + l32] = lt;
+    }
+    wait_lds();
+    barrier();
+    const int n_splits = a.ws_meta[4 * uu + 2];
+    const int split = a.ws_meta[4 * uu + 1] + (wg - a.ws_meta[4 * uu + 3]);
+#pragma unroll
+    for (int rb = 0; rb < R; rb++) {
+      const int r = 32 * rb + l32;
+      const float mf = mm[r], lf = ll[r];
+      if (r >= ui.rows) continue;
+      const bool empty = !(lf > 0.f);
+      const float inv = empty ? 0.f : 1.0f / lf;
+      const float lse2 = empty ? kNegInf : mf + __log2f(lf);
+      const bool lse_writer = g == 0 && rg == 0;
+      if (n_splits <= 1) {
+        uint16_t* dst = a.out + ((size_t)ui.row0 + r) * kDC + 4 * g;
+#pragma unroll
+        for (int dbl = 0; dbl < DB; dbl++) {
+          const int db = DB * rg + dbl;
+          const f32x16& ob = o[dbl * R + rb];
+#pragma unroll
+          for (int q = 0; q < 4; q++) {
+            bf16x2 p0 = {(__bf16)(acc_get(ob, 4 * q + 0) * inv), (__bf16)(acc_get(ob, 4 * q + 1) * inv)};
+            bf16x2 p1 = {(__bf16)(acc_get(ob, 4 * q + 2) * inv), (__bf16)(acc_get(ob, 4 * q + 3) * inv)};
+            u32x2 w = {__builtin_bit_cast(unsigned, p0), __builtin_bit_cast(unsigned, p1)};
+            *reinterpret_cast<u32x2*>(dst + 32 * db + 8 * q) = w;
+          }
+        }
+        if (lse_writer) a.lse[(size_t)ui.row0 + r] = empty ? kNegInf : lse2 * kLn2;
+      } else {
+        float* dst = a.ws_po + ((size_t)split * kMaxUnitRows + r) * kDC + 4 * g;
+#pragma unroll
+        for (int dbl = 0; dbl < DB; dbl++) {
+          const int db = DB * rg + dbl;
+          const f32x16& ob = o[dbl * R + rb];
+#pragma unroll
+          for (int q = 0; q < 4; q++) {
+            f32x4 w = {acc_get(ob, 4 * q) * inv, acc_get(ob, 4 * q + 1) * inv,
+                       acc_get(ob, 4 * q + 2) * inv, acc_get(ob, 4 * q + 3) * inv};
+            *reinterpret_cast<f32x4*>(dst + 32 * db + 8 * q) = w;
+          }
+        }
+        if (lse_writer) a.ws_plse[(size_t)split * kMaxUnitRows + r] = lse2;
+      }
+    }
+  };
+
+  // ------------------------------------------------------------ prologue
+#pragma unroll 1
+  for (int x = 0; x < W::kLeadCur; x++) {
+    lookup(x);
+    next();
+  }
+  wait_vm<0>();
+  wait_lds();
+  barrier();
+  if constexpr (SPARSE) {
+#pragma unroll 1
+    for (int y = 0; y < W::kLeadPage; y++) page_lookup(y);
+    wait_vm<0>();
+    wait_lds();
+    barrier();
+  }
+#pragma unroll 1
+  for (int z = 0; z < W::kLeadDma; z++) {
+    dummy_lookups();
+    copy_all(z);
+  }
+
+  // ------------------------------------------------------------ main loop
+  // One outer iteration per unit (segment); the inner loop runs its items.
+  // At a unit change the next unit's Q is requested before the finished
+  // unit's results are stored, so the loads do not queue behind the stores.
+  int s = 0;
+  wait_item();
+  wait_lds();
+  barrier();
+  Desc dc = read_desc(0);
+  Desc dz = read_desc(W::kLeadDma);
+  int uu = dc.u;
+  UnitInfo ui{};
+  if (uu >= 0) {
+    ui = unit_info(a, SPARSE, uu);
+    load_q(ui);
+    take_q();
+  }
+#pragma unroll 1
+  while (uu >= 0) {
+    reset();
+#pragma unroll 1
+    do {
+      lookup(s + W::kLeadCur);
+      next();
+      page_lookup(s + W::kLeadPage);
+      const int z = s + W::kLeadDma;
+      const Src sr = source(z, dz);
+      step(slots + (s % W::kSlots) * W::kSlotBytes, lds_addr(slots + (z % W::kSlots) * W::kSlotBytes),
+           sr, s, dc, ui);
+      s++;
+      wait_item();
+      wait_lds();
+      barrier();  // item s is in LDS for every wave; step s-1 is done everywhere
+      dc = read_desc(s);
+      dz = read_desc(s + W::kLeadDma);
+    } while (dc.u == uu);
+    const UnitInfo done = ui;
+    if (dc.u >= 0) {
+      ui = unit_info(a, SPARSE, dc.u);
+      load_q(ui);
+    }
+    end_segment(done, uu);
+    wait_lds();
+    barrier();  // the merge buffers are free again
+    take_q();
+    uu = dc.u;
+  }
+  wait_vm<0>();  // no copy may still be landing when the workgroup ends
+}
+
 // One entry point per (cache dtype, dense|sparse, wave shape).
 #define MLA_DECODE_KERNEL(NAME, FP8, SPARSE, R, T, NBUF)                         \
   __global__ __launch_bounds__(64 * R * T, 1) void NAME(DecodeArgs a) {          \
     decode_body<FP8, SPARSE, R, T, NBUF>(a);                                     \
   }
-MLA_DECODE_KERNEL(decode_bf16_dense_r4, false, false, 4, 1, 2)
-MLA_DECODE_KERNEL(decode_bf16_dense_r2, false, false, 2, 2, 1)
+#define MLA_WIDE_KERNEL(NAME, FP8, SPARSE, R)                                    \
+  __global__ __launch_bounds__(64 * R, 1) void NAME(DecodeArgs a) {              \
+    decode_wide<FP8, SPARSE, R>(a);                                              \
+  }
+MLA_WIDE_KERNEL(decode_bf16_dense_r4, false, false, 4)
+MLA_WIDE_KERNEL(decode_bf16_dense_r2, false, false, 2)
 MLA_DECODE_KERNEL(decode_bf16_dense_r1, false, false, 1, 2, 1)
-MLA_DECODE_KERNEL(decode_bf16_sparse_r4, false, true, 4, 1, 2)
-MLA_DECODE_KERNEL(decode_bf16_sparse_r2, false, true, 2, 2, 1)
+MLA_WIDE_KERNEL(decode_bf16_sparse_r4, false, true, 4)
+MLA_WIDE_KERNEL(decode_bf16_sparse_r2, false, true, 2)
 MLA_DECODE_KERNEL(decode_bf16_sparse_r1, false, true, 1, 2, 1)
-MLA_DECODE_KERNEL(decode_fp8_dense_r4, true, false, 4, 1, 2)
-MLA_DECODE_KERNEL(decode_fp8_dense_r2, true, false, 2, 2, 1)
+MLA_WIDE_KERNEL(decode_fp8_dense_r4, true, false, 4)
+MLA_WIDE_KERNEL(decode_fp8_dense_r2, true, false, 2)
 MLA_DECODE_KERNEL(decode_fp8_dense_r1, true, false, 1, 4, 1)
-MLA_DECODE_KERNEL(decode_fp8_sparse_r4, true, true, 4, 1, 2)
-MLA_DECODE_KERNEL(decode_fp8_sparse_r2, true, true, 2, 2, 1)
+MLA_WIDE_KERNEL(decode_fp8_sparse_r4, true, true, 4)
+MLA_WIDE_KERNEL(decode_fp8_sparse_r2, true, true, 2)
 MLA_DECODE_KERNEL(decode_fp8_sparse_r1, true, true, 1, 4, 1)
+#undef MLA_WIDE_KERNEL
 #undef MLA_DECODE_KERNEL
 
 // ---------------------------------------------------------------------------
@@ -771,26 +1546,37 @@ hipError_t launch_shape(void (*kern)(DecodeArgs), const Geometry& g, const Decod
   return hipGetLastError();
 }
 
+template <bool FP8, bool SPARSE, int R>
+hipError_t launch_wide(void (*kern)(DecodeArgs), const Geometry& g, const DecodeArgs& a,
+                       hipStream_t stream) {
+  using W = Wide<FP8, SPARSE, R>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, W::kLdsBytes);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(g.num_wg), dim3(W::kThreads), W::kLdsBytes, stream, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_variant(bool fp8, bool sparse, const Geometry& g, const DecodeArgs& a,
                           hipStream_t s) {
   const int shape = g.m_unit > 64 ? 4 : g.m_unit > 32 ? 2 : 1;
   if (!fp8 && !sparse) {
-    if (shape == 4) return launch_shape<false, false, 4, 1, 2>(decode_bf16_dense_r4, g, a, s);
-    if (shape == 2) return launch_shape<false, false, 2, 2, 1>(decode_bf16_dense_r2, g, a, s);
+    if (shape == 4) return launch_wide<false, false, 4>(decode_bf16_dense_r4, g, a, s);
+    if (shape == 2) return launch_wide<false, false, 2>(decode_bf16_dense_r2, g, a, s);
     return launch_shape<false, false, 1, 2, 1>(decode_bf16_dense_r1, g, a, s);
   }
   if (!fp8 && sparse) {
-    if (shape == 4) return launch_shape<false, true, 4, 1, 2>(decode_bf16_sparse_r4, g, a, s);
-    if (shape == 2) return launch_shape<false, true, 2, 2, 1>(decode_bf16_sparse_r2, g, a, s);
+    if (shape == 4) return launch_wide<false, true, 4>(decode_bf16_sparse_r4, g, a, s);
+    if (shape == 2) return launch_wide<false, true, 2>(decode_bf16_sparse_r2, g, a, s);
     return launch_shape<false, true, 1, 2, 1>(decode_bf16_sparse_r1, g, a, s);
   }
   if (!sparse) {
-    if (shape == 4) return launch_shape<true, false, 4, 1, 2>(decode_fp8_dense_r4, g, a, s);
-    if (shape == 2) return launch_shape<true, false, 2, 2, 1>(decode_fp8_dense_r2, g, a, s);
+    if (shape == 4) return launch_wide<true, false, 4>(decode_fp8_dense_r4, g, a, s);
+    if (shape == 2) return launch_wide<true, false, 2>(decode_fp8_dense_r2, g, a, s);
     return launch_shape<true, false, 1, 4, 1>(decode_fp8_dense_r1, g, a, s);
   }
-  if (shape == 4) return launch_shape<true, true, 4, 1, 2>(decode_fp8_sparse_r4, g, a, s);
-  if (shape == 2) return launch_shape<true, true, 2, 2, 1>(decode_fp8_sparse_r2, g, a, s);
+  if (shape == 4) return launch_wide<true, true, 4>(decode_fp8_sparse_r4, g, a, s);
+  if (shape == 2) return launch_wide<true, true, 2>(decode_fp8_sparse_r2, g, a, s);
   return launch_shape<true, true, 1, 4, 1>(decode_fp8_sparse_r1, g, a, s);
 }
 
@@ -812,6 +1598,8 @@ WsLayout ws_layout(const Geometry& g) {
   off = up(off + sizeof(float) * (size_t)g.max_splits * kMaxUnitRows);
   w.po = off;
   off = up(off + sizeof(float) * (size_t)g.max_splits * kMaxUnitRows * kDC);
+  w.zero = off;
+  off = up(off + 1280);
   w.total = off;
   return w;
 }

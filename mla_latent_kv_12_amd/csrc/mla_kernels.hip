@@ -44,10 +44,18 @@ constexpr float kLn2 = 0.693147180559945309f;
 // exceeds it by more than this (log2 units); exp2 values stay below 2^8.
 constexpr float kRescaleSlack = 8.0f;
 
+// Load of data that no kernel of the launch writes (sizes, schedule): through
+// the constant address space the compiler may use scalar loads, whose waits
+// do not also wait for the vector memory queue.
+template <typename T>
+__device__ __forceinline__ T ldc(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)reinterpret_cast<uintptr_t>(p);
+}
+
 __device__ __forceinline__ int unit_tiles(const DecodeArgs& a, bool sparse, int u) {
   if (sparse) return (a.topk + kPage - 1) / kPage;
   int su = u / a.row_blocks;
-  int L = a.seqlens[su];
+  int L = ldc(a.seqlens + su);
   return L > 0 ? (L + kPage - 1) / kPage : 0;
 }
 
@@ -64,7 +72,7 @@ __device__ __forceinline__ UnitInfo unit_info(const DecodeArgs& a, bool sparse, 
   x.rows = min(kMaxUnitRows, a.m_full - kMaxUnitRows * rb);
   x.rin_b0 = kMaxUnitRows * rb;           // first row of the unit inside its sequence unit
   x.row0 = su * a.m_full + x.rin_b0;      // flat row index of local row 0
-  int L = a.seqlens[x.b];
+  int L = ldc(a.seqlens + x.b);
   x.L = L > 0 ? L : 0;
   return x;
 }
@@ -1107,6 +1115,9 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
   // o[dbl * R + rb]: O^T for dims 32*(DB*rg + dbl) .., rows 32*rb + l32.
 
   auto load_q = [&](const UnitInfo& ui) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));  // as in end_segment
+    const int l32 = ln & 31, g = ln >> 5;
     const int r = rg * kRowsPerWave + l32;
     const bool ok = r < ui.rows;
     const size_t grow = (size_t)ui.row0 + (ok ? r : 0);
@@ -1344,6 +1355,12 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
   // Normalises this wave's dims of every row and writes them to out/lse
   // (unit finished here) or to the unit's split partials.
   auto end_segment = [&](const UnitInfo& ui, int uu) {
+    // Lane-derived offsets are recomputed here rather than kept live (and
+    // spilled) across the whole loop; a spill reload would wait for every
+    // copy in flight.
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int l32 = ln & 31, g = ln >> 5;
     const float lt = pair_sum(l_run);
     float* mm = mrg;
     float* ll = mrg + 32 * R;

@@ -21,7 +21,7 @@ constexpr int kTileFp8 = kPage * kBytesFp8Row;    // 36864
 // Scheduling constants: a split costs this many tiles of fixed work (query
 // load + partial write/read), and a workgroup is never given less work.
 constexpr int kSplitCost = 2;
-constexpr int kMinWgCost = 6;
+constexpr int kMinWgCost = 2;
 
 // Problem geometry after the host has folded (B, Sq, H, sparse) into units.
 // A "sequence unit" (su) is a set of query rows that attend over the same

@@ -82,12 +82,18 @@ __device__ __forceinline__ UnitInfo unit_info(const DecodeArgs& a, bool sparse, 
 // cost interval [g*Q, (g+1)*Q) with Q = max(ceil(total / G), kMinWgCost); a
 // tile belongs to the workgroup whose interval holds its cost position.
 // ---------------------------------------------------------------------------
+// Units whose cost prefix fits here are searched in LDS (a binary search in
+// global memory costs one memory round trip per level).
+constexpr int kPlanLdsUnits = 8192;
+
 template <bool SPARSE>
 __global__ __launch_bounds__(256) void plan_kernel(DecodeArgs a) {
   __shared__ int part[256];
+  __shared__ int c_lds[kPlanLdsUnits + 1];
   const int tid = threadIdx.x;
   const int U = a.n_units, G = a.num_wg;
   int32_t* C = a.ws_cost;
+  const bool in_lds = U <= kPlanLdsUnits;
   const int per = (U + 255) / 256;
   const int lo = min(U, tid * per), hi = min(U, lo + per);
 
@@ -104,10 +110,14 @@ __global__ __launch_bounds__(256) void plan_kernel(DecodeArgs a) {
   int run = part[tid] - s;
   for (int u = lo; u < hi; u++) {
     C[u] = run;
+    if (in_lds) c_lds[u] = run;
     run += unit_tiles(a, SPARSE, u) + kSplitCost;
   }
   const int total = part[255];
-  if (tid == 0) C[U] = total;
+  if (tid == 0) {
+    C[U] = total;
+    if (in_lds) c_lds[U] = total;
+  }
   // the zero row the main kernel copies in place of invisible cache rows
   if (tid < 1280 / 16) reinterpret_cast<i32x4*>(const_cast<uint8_t*>(a.ws_zero))[tid] = i32x4{0, 0, 0, 0};
   __threadfence_block();
@@ -121,10 +131,11 @@ __global__ __launch_bounds__(256) void plan_kernel(DecodeArgs a) {
       u = U;
       t = 0;
     } else {
+      const int* Cs = in_lds ? c_lds : C;
       int l = 0, h = U;  // C[l] <= x < C[h]
       while (h - l > 1) {
         int mid = (l + h) >> 1;
-        if (C[mid] <= x) l = mid; else h = mid;
+        if (Cs[mid] <= x) l = mid; else h = mid;
       }
       u = l;
       t = max(0, (int)(x - C[u]) - kSplitCost);
@@ -134,12 +145,13 @@ __global__ __launch_bounds__(256) void plan_kernel(DecodeArgs a) {
   }
 
   // splits per unit and their prefix
+  const int* Cs = in_lds ? c_lds : C;
   int ns_sum = 0;
   for (int u = lo; u < hi; u++) {
-    int n = C[u + 1] - C[u] - kSplitCost;
+    int n = Cs[u + 1] - Cs[u] - kSplitCost;
     int ns = 0;
     if (n > 0) {
-      int gf = (C[u] + kSplitCost) / Q, gl = (C[u] + kSplitCost + n - 1) / Q;
+      int gf = (Cs[u] + kSplitCost) / Q, gl = (Cs[u] + kSplitCost + n - 1) / Q;
       ns = gl - gf + 1;
     }
     ns_sum += ns;
@@ -155,11 +167,11 @@ __global__ __launch_bounds__(256) void plan_kernel(DecodeArgs a) {
   }
   int base = part[tid] - ns_sum;
   for (int u = lo; u < hi; u++) {
-    int n = C[u + 1] - C[u] - kSplitCost;
+    int n = Cs[u + 1] - Cs[u] - kSplitCost;
     int ns = 0, gf = -1;
     if (n > 0) {
-      gf = (C[u] + kSplitCost) / Q;
-      int gl = (C[u] + kSplitCost + n - 1) / Q;
+      gf = (Cs[u] + kSplitCost) / Q;
+      int gl = (Cs[u] + kSplitCost + n - 1) / Q;
       ns = gl - gf + 1;
     }
     a.ws_meta[4 * u + 0] = n;

@@ -65,7 +65,14 @@ bool make_geometry(int B, int Sq, int H, int topk, int num_wg, mla::Geometry* g)
   return true;
 }
 
-int resolve_wg(int num_wg) { return num_wg > 0 ? num_wg : device_cus(); }
+// Workgroup count: the caller's, or one per compute unit (two for units of
+// at most 32 query rows, whose one-wave workgroups fit two to a unit).
+int resolve_wg(int num_wg, int Sq, int H, int topk) {
+  if (num_wg > 0) return num_wg;
+  const long long rows = topk > 0 ? (long long)H : (long long)Sq * H;
+  const int cus = device_cus();
+  return rows <= 32 ? 2 * cus : cus;
+}
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -116,7 +123,7 @@ mla_status run(const void* q_nope, const void* q_rope, const void* kv_pages, con
     return fail(MLA_ERR_ALIGN, "tensor pointer misaligned (16 B for q/kv/scales/out, 4 B for the rest)");
   if (!workspace) return fail(MLA_ERR_WORKSPACE, "workspace is NULL");
   if (!aligned(workspace, 256)) return fail(MLA_ERR_ALIGN, "workspace must be 256-byte aligned");
-  const int wg = resolve_wg(num_wg);
+  const int wg = resolve_wg(num_wg, Sq, H, topk);
   if (wg <= 0) return fail(MLA_ERR_HIP, "could not query the device's compute units");
   mla::Geometry g;
   if (!make_geometry(B, Sq, H, topk, wg, &g)) return fail(MLA_ERR_SHAPE, "sizes out of range");
@@ -165,7 +172,7 @@ extern "C" {
 size_t mla_workspace_size(int B, int Sq, int H, int topk, int num_wg) {
   mla::Geometry g;
   if (num_wg < 0 || num_wg > kMaxWg) return 0;
-  const int wg = resolve_wg(num_wg);
+  const int wg = resolve_wg(num_wg, Sq, H, topk);
   if (wg <= 0 || !make_geometry(B, Sq, H, topk, wg, &g)) return 0;
   return mla::ws_layout(g).total;
 }
@@ -179,7 +186,7 @@ mla_status mla_plan(const int32_t* cache_seqlens, int B, int Sq, int H, int topk
   if (!aligned(cache_seqlens, 4)) return fail(MLA_ERR_ALIGN, "cache_seqlens must be 4-byte aligned");
   if (B <= 0 || Sq <= 0 || H <= 0 || topk < 0) return fail(MLA_ERR_SHAPE, "B, Sq, H must be >= 1 and topk >= 0");
   if (num_wg < 0 || num_wg > kMaxWg) return fail(MLA_ERR_SHAPE, "num_wg out of range [0, %d]", kMaxWg);
-  const int wg = resolve_wg(num_wg);
+  const int wg = resolve_wg(num_wg, Sq, H, topk);
   if (wg <= 0) return fail(MLA_ERR_HIP, "could not query the device's compute units");
   mla::Geometry g;
   if (!make_geometry(B, Sq, H, topk, wg, &g)) return fail(MLA_ERR_SHAPE, "sizes out of range");
@@ -243,7 +250,7 @@ mla_status mla_combine(const int32_t* cache_seqlens, int B, int Sq, int H, int t
     return fail(MLA_ERR_ALIGN, "tensor pointer misaligned (16 B for out, 4 B for the rest)");
   if (B <= 0 || Sq <= 0 || H <= 0 || topk < 0) return fail(MLA_ERR_SHAPE, "B, Sq, H must be >= 1 and topk >= 0");
   if (num_wg < 0 || num_wg > kMaxWg) return fail(MLA_ERR_SHAPE, "num_wg out of range [0, %d]", kMaxWg);
-  const int wg = resolve_wg(num_wg);
+  const int wg = resolve_wg(num_wg, Sq, H, topk);
   if (wg <= 0) return fail(MLA_ERR_HIP, "could not query the device's compute units");
   mla::Geometry g;
   if (!make_geometry(B, Sq, H, topk, wg, &g)) return fail(MLA_ERR_SHAPE, "sizes out of range");

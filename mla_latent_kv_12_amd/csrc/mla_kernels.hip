@@ -10,16 +10,19 @@
 //
 //   plan_kernel     split-KV partition of all 64-token tiles over the
 //                   persistent workgroups, with a fixed cost per split
-//   decode_kernel   per workgroup: stream its tiles HBM -> LDS (direct
-//                   global->LDS loads, XOR-swizzled rows), S^T = K Q^T and
-//                   O^T += V^T P^T on bf16 MFMA 32x32x16 with fp32
-//                   accumulation, online softmax in the log2 domain; fp8 e4m3
-//                   tiles are converted to bf16 in registers (exact)
+//   decode_*_r{4,2,1w}
+//                   per workgroup: stream its 32-token chunks HBM -> LDS
+//                   (direct global->LDS loads into a ring of slots,
+//                   XOR-swizzled rows), S^T = K Q^T and O^T += V^T P^T on
+//                   bf16 MFMA 32x32x16 with fp32 accumulation, online softmax
+//                   in the log2 domain; fp8 e4m3 chunks are converted to bf16
+//                   in registers (exact)
 //   combine_kernel  log-sum-exp merge of the partial results of split units
 //
-// Wave roles: a wave owns 32 query rows and one "token lane".  R waves with
-// different rows share each LDS tile (R = 4 for 128 rows); T token lanes work
-// on different tiles of the same unit and are merged at the end of the unit.
+// Wave roles: the R waves of a workgroup (R = 4, 2, 1 for units of up to
+// 128, 64, 32 query rows) share each chunk in LDS.  For the scores a wave
+// owns 32 query rows; for P.V it owns 512/R output dims of all the unit's
+// rows.  One-wave workgroups run two to a compute unit.
 #include "mla_internal.h"
 
 #include <utility>
@@ -182,52 +185,6 @@ __global__ __launch_bounds__(256) void plan_kernel(DecodeArgs a) {
   }
 }
 
-// ---------------------------------------------------------------------------
-// Main kernel
-//
-// LDS tile layout (one "slot" per buffered tile):
-//   region A  [64 rows][512 latent dims]  c part: 1024 B (bf16) | 512 B (fp8) per row
-//   region B  [64 rows][64 rope dims]     k_rope part: 128 B | 64 B per row
-//   scales    [64] fp32 (fp8 only), then a 16-byte meta word
-// Inside a row the 16-byte chunk c is stored at position c ^ (row & 7)
-// (c ^ (row & 3) in the 4-chunk fp8 rope rows), so the 32 lanes that read
-// one chunk of 32 consecutive rows hit different banks.  A region-A row of
-// bf16 is exactly one wave-wide 16-byte-per-lane copy, so the HBM->LDS copy
-// of a row is one direct global->LDS instruction with contiguous 1 KB
-// source and destination.
-// ---------------------------------------------------------------------------
-template <bool FP8, bool SPARSE, int R, int T, int NBUF>
-struct Shape {
-  static constexpr int kThreads = 64 * R * T;
-  static constexpr int kEB = FP8 ? 1 : 2;               // bytes per cached element
-  static constexpr int kRowBytes = kD * kEB;            // 1152 | 576 bytes per token in HBM
-  static constexpr int kABytes = kDC * kEB;             // 1024 | 512
-  static constexpr int kBBytes = kDR * kEB;             // 128 | 64
-  static constexpr int kRegionB = kPage * kABytes;      // 65536 | 32768
-  static constexpr int kTileBytes = kPage * kRowBytes;  // 73728 | 36864
-  static constexpr int kAChunks = kABytes / 16;         // 64 | 32
-  static constexpr int kBChunks = kBBytes / 16;         // 8 | 4
-  static constexpr int kAInstr = kPage * kAChunks / 64; // 64 | 32 wave-wide copies
-  static constexpr int kBInstr = kPage * kBChunks / 64; // 8 | 4
-  static constexpr int kAIters = kAInstr / R;
-  static constexpr int kBIters = kBInstr / R;
-  static constexpr int kSlotBytes = kTileBytes + 256 + 16;  // tile | scales | meta
-  static constexpr int kSlotsBytes = T * NBUF * kSlotBytes;
-  static constexpr int kXchgBytes = (T > 1) ? R * (T / 2) * 65536 : 0;
-  static constexpr int kBigBytes = kSlotsBytes > kXchgBytes ? kSlotsBytes : kXchgBytes;
-  static constexpr int kRowTabOff = kBigBytes;
-  static constexpr int kRowTabBytes = SPARSE ? T * 64 * 8 : 0;
-  static constexpr int kMergeOff = kRowTabOff + kRowTabBytes;
-  static constexpr int kMergeBytes = (T > 1) ? 2 * R * T * 32 * 4 : 0;
-  static constexpr int kLdsBytes = kMergeOff + kMergeBytes;
-  static_assert(kAInstr % R == 0 && kBInstr % R == 0, "copies must split evenly over loader waves");
-  static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
-};
-
-__device__ __forceinline__ void wait_loads() {
-  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-}
-
 __device__ __forceinline__ bf16x8 cvt8_fp8(u32x2 v) {
   bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[0], 1.0f, false);
   bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[0], 1.0f, true);
@@ -262,483 +219,17 @@ __device__ __forceinline__ void acc_scale(f32x16& v, float s) {
         : "v"(s));
   }
 }
-__device__ __forceinline__ void acc_add(f32x16& v, int i, float x) {
-  float t;
-  asm("v_accvgpr_read_b32 %1, %0\n\tv_add_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
-      : "+a"(v[i]), "=&v"(t)
-      : "v"(x));
-}
 __device__ __forceinline__ float acc_get(const f32x16& v, int i) {
   float t;
   asm("v_accvgpr_read_b32 %0, %1" : "=v"(t) : "a"(v[i]));
   return t;
 }
-// v *= s when the wave-uniform flag is nonzero.  The branch is inside the
-// assembly so the compiler sees one unconditional update of the block and
-// keeps it in place (a visible branch makes it copy the accumulators).
-__device__ __forceinline__ void acc_scale_if(f32x16& v, float s, int flag) {
-  float t;
-#define MLA_SCL(i) "v_accvgpr_read_b32 %16, %" #i "\n\tv_mul_f32 %16, %16, %17\n\tv_accvgpr_write_b32 %" #i ", %16\n\t"
-  asm volatile(
-      "s_cmp_eq_u32 %18, 0\n\t"
-      "s_cbranch_scc1 1f\n\t"
-      MLA_SCL(0) MLA_SCL(1) MLA_SCL(2) MLA_SCL(3) MLA_SCL(4) MLA_SCL(5) MLA_SCL(6) MLA_SCL(7)
-      MLA_SCL(8) MLA_SCL(9) MLA_SCL(10) MLA_SCL(11) MLA_SCL(12) MLA_SCL(13) MLA_SCL(14) MLA_SCL(15)
-      "1:"
-      : "+a"(v[0]), "+a"(v[1]), "+a"(v[2]), "+a"(v[3]), "+a"(v[4]), "+a"(v[5]), "+a"(v[6]),
-        "+a"(v[7]), "+a"(v[8]), "+a"(v[9]), "+a"(v[10]), "+a"(v[11]), "+a"(v[12]), "+a"(v[13]),
-        "+a"(v[14]), "+a"(v[15]), "=&v"(t)
-      : "v"(s), "s"(flag));
-#undef MLA_SCL
-}
-
 // Workgroup i is dispatched to XCD i % 8; give each XCD a contiguous range
 // of logical workgroups so neighbours (which share sequences and their
 // query rows) share an L2.
 __device__ __forceinline__ int xcd_logical(int i, int G) {
   int q = G >> 3, r = G & 7, x = i & 7, k = i >> 3;
   return x * q + min(x, r) + k;
-}
-
-template <bool FP8, bool SPARSE, int R, int T, int NBUF>
-__device__ __forceinline__ void decode_body(const DecodeArgs& a) {
-  using S = Shape<FP8, SPARSE, R, T, NBUF>;
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int rg = wave % R, tl = wave / R;
-  const int g = lane >> 5, l32 = lane & 31;
-  const int wg = xcd_logical(blockIdx.x, gridDim.x);
-
-  int u = a.ws_work[2 * wg], lo = a.ws_work[2 * wg + 1];
-  const int u_end = a.ws_work[2 * wg + 2], t_end = a.ws_work[2 * wg + 3];
-
-  // Current segment [lo, hi) of unit u; false once the range is exhausted.
-  auto settle = [&](int& uu, int& ll, int& hh) -> bool {
-    for (;;) {
-      if (uu > u_end || uu >= a.n_units) return false;
-      hh = (uu == u_end) ? t_end : a.ws_meta[4 * uu];
-      if (ll < hh) return true;
-      uu++;
-      ll = 0;
-    }
-  };
-  int hi = 0;
-  if (!settle(u, lo, hi)) return;  // uniform over the workgroup
-
-  uint8_t* slots = lds;
-  int64_t* rowtab = reinterpret_cast<int64_t*>(lds + S::kRowTabOff);
-  float* mrg = reinterpret_cast<float*>(lds + S::kMergeOff);
-
-  // -------------------------------------------------------------- loads
-  // Copy lane tl's tile of round `rho` of segment (uu, ll, hh) into buffer
-  // `buf`.  Called by every wave (the sparse path has a barrier inside).
-  auto issue = [&](int uu, int ll, int hh, int rho, int buf) {
-    const int tile = ll + rho * T + tl;
-    const bool has = tile < hh;
-    uint8_t* slot = slots + (tl * NBUF + buf) * S::kSlotBytes;
-    int* meta = reinterpret_cast<int*>(slot + S::kTileBytes + 256);
-    const UnitInfo ui = unit_info(a, SPARSE, uu);
-    const uint8_t* page_base = nullptr;
-    int nvalid = 0;
-    unsigned long long vmask = 0;
-    if constexpr (!SPARSE) {
-      if (!has) return;
-      nvalid = min(kPage, ui.L - kPage * tile);
-      const int page = tile < a.bt_stride ? a.block_table[(size_t)ui.b * a.bt_stride + tile] : -1;
-      if (page < 0 || page >= a.num_pages) nvalid = 0;
-      if (rg == 0 && lane == 0) meta[0] = nvalid;
-      if (nvalid <= 0) return;
-      page_base = a.kv + (size_t)page * S::kTileBytes;
-      if constexpr (FP8) {
-        if (rg == 0 && lane < 16)
-          __builtin_amdgcn_global_load_lds(a.kv_scales + (size_t)page * kPage + lane * 4,
-                                           (LDS_AS void*)(slot + S::kTileBytes), 16, 0, 0);
-      }
-    } else {
-      if (has && rg == 0) {
-        const int e = tile * kPage + lane;
-        const int su = ui.row0 / a.m_full;
-        const int idx = e < a.topk ? a.indices[(size_t)su * a.topk + e] : -1;
-        bool ok = idx >= 0 && idx < ui.L && (idx >> 6) < a.bt_stride;
-        const int page = ok ? a.block_table[(size_t)ui.b * a.bt_stride + (idx >> 6)] : -1;
-        ok = ok && page >= 0 && page < a.num_pages;
-        const int64_t tok = ok ? (int64_t)page * kPage + (idx & 63) : 0;
-        rowtab[tl * 64 + lane] = tok;
-        const unsigned long long m = __ballot(ok);
-        if (lane == 0) {
-          meta[0] = (int)(m & 0xffffffffull);
-          meta[1] = (int)(m >> 32);
-        }
-        if constexpr (FP8) {
-          if (ok)
-            __builtin_amdgcn_global_load_lds(a.kv_scales + tok, (LDS_AS void*)(slot + S::kTileBytes), 4, 0, 0);
-        }
-      }
-      __syncthreads();
-      if (!has) return;
-      vmask = (unsigned long long)(unsigned)__builtin_amdgcn_readfirstlane(meta[0]) |
-              ((unsigned long long)(unsigned)__builtin_amdgcn_readfirstlane(meta[1]) << 32);
-    }
-    auto row_ok = [&](int row) -> bool {
-      if constexpr (SPARSE) return (vmask >> row) & 1ull;
-      else return row < nvalid;
-    };
-    // Source of chunk c of row `row`: dense rows are contiguous in the page,
-    // sparse rows come from the row table.
-    auto src_of = [&](int row, int byte_in_row) -> const uint8_t* {
-      if constexpr (SPARSE) return a.kv + rowtab[tl * 64 + row] * S::kRowBytes + byte_in_row;
-      else return page_base + row * S::kRowBytes + byte_in_row;
-    };
-    const i32x4 zero = {0, 0, 0, 0};
-    // region A: latent part of each row.  bf16: copy j is row j, lane = chunk
-    // position; fp8: copy j is rows 2j and 2j+1, 32 lanes each.
-#pragma unroll
-    for (int it = 0; it < S::kAIters; it++) {
-      const int j = it * R + rg;
-      uint8_t* dst = slot + j * 1024;
-      int row, byte;
-      if constexpr (!FP8) {
-        row = j;
-        byte = (lane ^ (j & 7)) << 4;
-      } else {
-        const int hl = lane >> 5;
-        row = 2 * j + hl;
-        byte = ((lane & 31) ^ ((2 * j + hl) & 7)) << 4;
-      }
-      if (row_ok(row))
-        __builtin_amdgcn_global_load_lds(src_of(row, byte), (LDS_AS void*)dst, 16, 0, 0);
-      else
-        *reinterpret_cast<i32x4*>(dst + lane * 16) = zero;
-    }
-    // region B: RoPE part.  bf16: copy j is rows 8j..8j+7 (8 lanes each);
-    // fp8: rows 16j..16j+15 (4 lanes each).
-#pragma unroll
-    for (int it = 0; it < S::kBIters; it++) {
-      const int j = it * R + rg;
-      uint8_t* dst = slot + S::kRegionB + j * 1024;
-      int row, byte;
-      if constexpr (!FP8) {
-        row = 8 * j + (lane >> 3);
-        byte = S::kABytes + (((lane & 7) ^ ((lane >> 3) & 7)) << 4);
-      } else {
-        row = 16 * j + (lane >> 2);
-        byte = S::kABytes + (((lane & 3) ^ ((lane >> 2) & 3)) << 4);
-      }
-      if (row_ok(row))
-        __builtin_amdgcn_global_load_lds(src_of(row, byte), (LDS_AS void*)dst, 16, 0, 0);
-      else
-        *reinterpret_cast<i32x4*>(dst + lane * 16) = zero;
-    }
-  };
-
-  // -------------------------------------------------------------- state
-  bf16x8 qf[36];
-  f32x16 o[16];
-  float m_run = kNegInf, l_run = 0.f;
-
-  auto load_q = [&](const UnitInfo& ui) {
-    const int r = rg * kRowsPerWave + l32;
-    const bool ok = r < ui.rows;
-    const size_t grow = (size_t)ui.row0 + (ok ? r : 0);
-    const bf16x8* qn = reinterpret_cast<const bf16x8*>(a.q_nope + grow * kDC + 8 * g);
-    const bf16x8* qr = reinterpret_cast<const bf16x8*>(a.q_rope + grow * kDR + 8 * g);
-#pragma unroll
-    for (int ks = 0; ks < 32; ks++) qf[ks] = qn[2 * ks];
-#pragma unroll
-    for (int ks = 0; ks < 4; ks++) qf[32 + ks] = qr[2 * ks];
-    if (!ok) {  // padding rows of a unit with fewer than 32*R rows
-#pragma unroll
-      for (int ks = 0; ks < 36; ks++) qf[ks] = bf16x8{};
-    }
-  };
-  auto reset = [&]() {
-#pragma unroll
-    for (int i = 0; i < 16; i++) o[i] = f32x16{};
-    m_run = kNegInf;
-    l_run = 0.f;
-  };
-
-  // Per-lane pieces of the swizzled LDS addresses.
-  // K operand (S^T = K Q^T): token t = 32*half + l32, 8-dim group 2*ks + g.
-  const int kx_sw = g ^ (l32 & 7);
-  // V^T operand through transpose reads (see compute()).
-  const int G16 = lane >> 4, i16 = lane & 15;
-  int voff[4];
-  if constexpr (!FP8) {
-    // lane loads token 16ks + 8r + z, dims 32db + 16(G16&1) + 4(i16&3) .. +3
-    const int z = 4 * (G16 >> 1) + (i16 >> 2);
-    const int w = 2 * (G16 & 1) + ((i16 >> 1) & 1);
-#pragma unroll
-    for (int par = 0; par < 2; par++) voff[par] = z * 1024 + (((4 * par + w) ^ z) << 4) + 8 * (i16 & 1);
-    voff[2] = voff[3] = 0;
-  } else {
-    // lane loads token 16ks + 8(i16>>3) + z8, bytes 32db + 16(G16&1) + 8(i16&1) .. +7
-    const int z8 = 4 * (G16 >> 1) + ((i16 >> 1) & 3);
-    const int trow = 8 * (i16 >> 3) + z8;
-#pragma unroll
-    for (int p4 = 0; p4 < 4; p4++)
-      voff[p4] = trow * 512 + (((2 * p4 + (G16 & 1)) ^ z8) << 4) + 8 * (i16 & 1);
-  }
-
-  // -------------------------------------------------------------- compute
-  auto compute = [&](const uint8_t* slot, int tile, const UnitInfo& ui) {
-    const int* meta = reinterpret_cast<const int*>(slot + S::kTileBytes + 256);
-    int lim = 0;                 // dense: token tau is visible iff tau < lim
-    unsigned long long vm = 0;   // sparse: visibility bits, shifted by 4*g
-    if constexpr (!SPARSE) {
-      const int nvalid = __builtin_amdgcn_readfirstlane(meta[0]);
-      if (nvalid <= 0) return;
-      lim = nvalid;
-      if (a.causal) {
-        const int s = (ui.rin_b0 + rg * kRowsPerWave + l32) / a.H;
-        lim = min(lim, ui.L - a.Sq + s + 1 - kPage * tile);
-      }
-    } else {
-      vm = (unsigned long long)(unsigned)__builtin_amdgcn_readfirstlane(meta[0]) |
-           ((unsigned long long)(unsigned)__builtin_amdgcn_readfirstlane(meta[1]) << 32);
-      if (vm == 0) return;
-      vm >>= 4 * g;
-    }
-
-    // The tile is processed as two 32-token halves so that only one S^T
-    // block (16 fp32) and its P (8 bf16 pairs) are live beside Q and O.
-#pragma unroll 1
-    for (int half = 0; half < 2; half++) {
-      const int t = 32 * half + l32;
-      // ---- S^T[token][row] = K . Q^T over 576 dims for tokens 32*half + 0..31
-      f32x16 sacc = {};
-      if constexpr (!FP8) {
-        const uint8_t* ka = slot + t * 1024;
-        const uint8_t* kb = slot + S::kRegionB + t * 128;
-#pragma unroll
-        for (int ks = 0; ks < 36; ks++) {
-          const int c = ks < 32 ? 128 * (ks >> 2) + (((2 * (ks & 3)) ^ kx_sw) << 4)
-                                : (((2 * (ks - 32)) ^ kx_sw) << 4);
-          const bf16x8 kf = *reinterpret_cast<const bf16x8*>((ks < 32 ? ka : kb) + c);
-          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc, 0, 0, 0);
-        }
-      } else {
-        const uint8_t* ka = slot + t * 512 + 8 * g;
-        const uint8_t* kb = slot + S::kRegionB + t * 64 + 8 * g;
-#pragma unroll
-        for (int ks = 0; ks < 36; ks++) {
-          const int c = ks < 32 ? 128 * (ks >> 3) + (((ks & 7) ^ (l32 & 7)) << 4)
-                                : (((ks - 32) ^ (l32 & 3)) << 4);
-          const bf16x8 kf = cvt8_fp8(*reinterpret_cast<const u32x2*>((ks < 32 ? ka : kb) + c));
-          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc, 0, 0, 0);
-        }
-      }
-
-      // ---- online softmax; lane holds row l32 and tokens
-      //      32*half + 8*(i/4) + 4*g + i%4, i = 0..15
-      // fp8: token scales sigma_j (zero for invisible tokens) multiply the
-      // scores and, before the P.V product, the probabilities.
-      const float* scl = reinterpret_cast<const float*>(slot + S::kTileBytes) + 32 * half + 4 * g;
-      float mloc = kNegInf;
-#pragma unroll
-      for (int q4 = 0; q4 < 4; q4++) {
-        f32x4 sv = {1.f, 1.f, 1.f, 1.f};
-        if constexpr (FP8) sv = *reinterpret_cast<const f32x4*>(scl + 8 * q4);
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-          const int i = 4 * q4 + e;
-          const int tau_rel = 32 * half + 8 * q4 + e;  // token minus 4*g
-          float v = sacc[i] * a.scale_log2;
-          bool ok;
-          if constexpr (!SPARSE) ok = tau_rel + 4 * g < lim;
-          else ok = (vm >> tau_rel) & 1ull;
-          if constexpr (FP8) v *= ok ? sv[e] : 0.f;
-          sacc[i] = ok ? v : kNegInf;
-          mloc = fmaxf(mloc, sacc[i]);
-        }
-      }
-      const float mt = pair_max(mloc);
-      const float mnew = fmaxf(m_run, mt);
-      const bool need = mnew > m_run + kRescaleSlack;  // -inf + slack = -inf
-      if (__builtin_amdgcn_ballot_w64(need)) {
-        const float alpha = (m_run == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m_run - mnew);
-#pragma unroll
-        for (int d = 0; d < 16; d++) acc_scale(o[d], alpha);
-        l_run *= alpha;
-        m_run = mnew;
-      }
-      const float muse = (m_run == kNegInf) ? 0.f : m_run;
-      float psum = 0.f;
-      bf16x8 pf[2];
-#pragma unroll
-      for (int q4 = 0; q4 < 4; q4++) {
-        f32x4 sv = {1.f, 1.f, 1.f, 1.f};
-        if constexpr (FP8) sv = *reinterpret_cast<const f32x4*>(scl + 8 * q4);
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-          const int i = 4 * q4 + e;
-          float p = __builtin_amdgcn_exp2f(sacc[i] - muse);
-          psum += p;
-          if constexpr (FP8) p *= (sacc[i] == kNegInf) ? 0.f : sv[e];
-          pf[i >> 3][i & 7] = (__bf16)p;
-        }
-      }
-      l_run += psum;
-
-      // ---- O^T[dim][row] += V^T[dim][token] . P^T[token][row]
-      // k-step ks = 2*half + kk covers tokens 16ks..16ks+15; lane half g
-      // holds tokens {16ks + 4g + 0..3} then {16ks + 8 + 4g + 0..3}, the
-      // same tokens its S^T accumulator rows hold, so P needs no
-      // cross-lane movement.  The transpose reads give lane l the dim
-      // 32db + l%32 of those 8 tokens.
-#pragma unroll
-      for (int kk = 0; kk < 2; kk++) {
-        const int ks = 2 * half + kk;
-#pragma unroll
-        for (int db = 0; db < 16; db++) {
-          bf16x8 v;
-          if constexpr (!FP8) {
-            const uint8_t* p = slot + voff[db & 1] + (16 * ks) * 1024 + (db >> 1) * 128;
-            i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(p));
-            i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(p + 8 * 1024));
-            i16x8 vv = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-            v = __builtin_bit_cast(bf16x8, vv);
-          } else {
-            const uint8_t* p = slot + voff[db & 3] + (16 * ks) * 512 + (db >> 2) * 128;
-            i32x2 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS i32x2*)(p));
-            v = cvt8_fp8(__builtin_bit_cast(u32x2, w));
-          }
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v, pf[kk], o[db], 0, 0, 0);
-        }
-      }
-    }
-  };
-
-  // -------------------------------------------------------------- epilogue
-  // Lane holds row r = 32*rg + l32 and dims 32*db + 8*q + 4*g + e of O.
-  auto finish = [&](const UnitInfo& ui, int uu, float mf, float lf) {
-    const int r = rg * kRowsPerWave + l32;
-    if (r >= ui.rows) return;
-    const int n_splits = a.ws_meta[4 * uu + 2];
-    const bool empty = !(lf > 0.f);
-    const float inv = empty ? 0.f : 1.0f / lf;
-    const float lse2 = empty ? kNegInf : mf + __log2f(lf);
-    if (n_splits <= 1) {
-      uint16_t* dst = a.out + ((size_t)ui.row0 + r) * kDC + 4 * g;
-#pragma unroll
-      for (int db = 0; db < 16; db++)
-#pragma unroll
-        for (int q = 0; q < 4; q++) {
-          bf16x2 p0 = {(__bf16)(acc_get(o[db], 4 * q + 0) * inv), (__bf16)(acc_get(o[db], 4 * q + 1) * inv)};
-          bf16x2 p1 = {(__bf16)(acc_get(o[db], 4 * q + 2) * inv), (__bf16)(acc_get(o[db], 4 * q + 3) * inv)};
-          u32x2 w = {__builtin_bit_cast(unsigned, p0), __builtin_bit_cast(unsigned, p1)};
-          *reinterpret_cast<u32x2*>(dst + 32 * db + 8 * q) = w;
-        }
-      if (g == 0) a.lse[(size_t)ui.row0 + r] = empty ? kNegInf : lse2 * kLn2;
-    } else {
-      const int split = a.ws_meta[4 * uu + 1] + (wg - a.ws_meta[4 * uu + 3]);
-      float* dst = a.ws_po + ((size_t)split * kMaxUnitRows + r) * kDC + 4 * g;
-#pragma unroll
-      for (int db = 0; db < 16; db++)
-#pragma unroll
-        for (int q = 0; q < 4; q++) {
-          f32x4 w = {acc_get(o[db], 4 * q) * inv, acc_get(o[db], 4 * q + 1) * inv,
-                     acc_get(o[db], 4 * q + 2) * inv, acc_get(o[db], 4 * q + 3) * inv};
-          *reinterpret_cast<f32x4*>(dst + 32 * db + 8 * q) = w;
-        }
-      if (g == 0) a.ws_plse[(size_t)split * kMaxUnitRows + r] = lse2;
-    }
-  };
-
-  auto end_segment = [&](const UnitInfo& ui, int uu) {
-    const float lt = pair_sum(l_run);
-    if constexpr (T == 1) {
-      finish(ui, uu, m_run, lt);
-    } else {
-      __syncthreads();  // every wave is done with the tiles: LDS reusable
-      float* mm = mrg;  // [R][T][32]
-      float* ll = mrg + R * T * 32;
-      if (g == 0) {
-        mm[(rg * T + tl) * 32 + l32] = m_run;
-        ll[(rg * T + tl) * 32 + l32] = lt;
-      }
-      __syncthreads();
-      float mf = kNegInf;
-#pragma unroll
-      for (int k = 0; k < T; k++) mf = fmaxf(mf, mm[(rg * T + k) * 32 + l32]);
-      float lf = 0.f;
-#pragma unroll
-      for (int k = 0; k < T; k++) {
-        const float mk = mm[(rg * T + k) * 32 + l32];
-        lf += (mk == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(mk - mf) * ll[(rg * T + k) * 32 + l32];
-      }
-      const float f = (m_run == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m_run - mf);
-#pragma unroll
-      for (int d = 0; d < 16; d++) acc_scale(o[d], f);
-      float* xb = reinterpret_cast<float*>(lds);
-      auto put = [&](int k) {
-        float* p = xb + (size_t)k * 16384 + lane;
-#pragma unroll
-        for (int d = 0; d < 16; d++)
-#pragma unroll
-          for (int i = 0; i < 16; i++) p[(d * 16 + i) * 64] = acc_get(o[d], i);
-      };
-      auto add = [&](int k) {
-        const float* p = xb + (size_t)k * 16384 + lane;
-#pragma unroll
-        for (int d = 0; d < 16; d++)
-#pragma unroll
-          for (int i = 0; i < 16; i++) acc_add(o[d], i, p[(d * 16 + i) * 64]);
-      };
-      if constexpr (T == 2) {
-        if (tl == 1) put(rg);
-        __syncthreads();
-        if (tl == 0) add(rg);
-      } else {
-        static_assert(T == 4, "token lanes");
-        if (tl >= 2) put(rg * 2 + (tl - 2));
-        __syncthreads();
-        if (tl < 2) add(rg * 2 + tl);
-        __syncthreads();
-        if (tl == 1) put(rg * 2);
-        __syncthreads();
-        if (tl == 0) add(rg * 2);
-      }
-      if (tl == 0) finish(ui, uu, mf, lf);
-    }
-  };
-
-  // -------------------------------------------------------------- main loop
-  // Segments (one unit each) in order; inside a segment, rounds of T tiles.
-  // With two buffers the next round's tiles (possibly the next segment's)
-  // are in flight while the current round is computed.
-  int rglob = 0;  // rounds processed by this workgroup
-  if constexpr (NBUF == 2) issue(u, lo, hi, 0, 0);
-  for (;;) {
-    const UnitInfo cu = unit_info(a, SPARSE, u);
-    load_q(cu);
-    reset();
-    const int nrounds = (hi - lo + T - 1) / T;
-    int nu = u + 1, nlo = 0, nhi = 0;
-    const bool more = settle(nu, nlo, nhi);
-    for (int rho = 0; rho < nrounds; rho++, rglob++) {
-      if constexpr (NBUF == 1) {
-        __syncthreads();  // previous round's readers are done
-        issue(u, lo, hi, rho, 0);
-      }
-      wait_loads();
-      __syncthreads();
-      const int buf = (NBUF == 2) ? (rglob & 1) : 0;
-      if constexpr (NBUF == 2) {
-        if (rho + 1 < nrounds) issue(u, lo, hi, rho + 1, buf ^ 1);
-        else if (more) issue(nu, nlo, nhi, 0, buf ^ 1);
-      }
-      const int tile = lo + rho * T + tl;
-      if (tile < hi) compute(slots + (tl * NBUF + buf) * S::kSlotBytes, tile, cu);
-    }
-    end_segment(cu, u);
-    if (!more) break;
-    u = nu;
-    lo = nlo;
-    hi = nhi;
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -861,7 +352,9 @@ struct Wide {
   static constexpr int kRegB = kRows * kABytes;     // region B (RoPE part) offset
   static constexpr int kScaleOff = kRegB + kRows * kDR * kEB;
   static constexpr int kSlotBytes = kScaleOff + (FP8 ? 128 : 0);
-  static constexpr int kSlots = 4;
+  // Two workgroups of one wave share a compute unit for units of <= 32 rows,
+  // so a bf16 one-wave workgroup keeps two chunks in flight instead of four.
+  static constexpr int kSlots = (R == 1 && !FP8) ? 2 : 4;
   static constexpr int kNA = FP8 ? 16 : 32;         // 1 KB copies of region A
   static constexpr int kNB = FP8 ? 2 : 4;           // 1 KB copies of region B
   static constexpr int kNCopy = kNA + kNB + (FP8 ? 1 : 0);  // (+ the 32 scales)
@@ -1499,28 +992,23 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
 }
 
 // One entry point per (cache dtype, dense|sparse, wave shape).
-#define MLA_DECODE_KERNEL(NAME, FP8, SPARSE, R, T, NBUF)                         \
-  __global__ __launch_bounds__(64 * R * T, 1) void NAME(DecodeArgs a) {          \
-    decode_body<FP8, SPARSE, R, T, NBUF>(a);                                     \
-  }
 #define MLA_WIDE_KERNEL(NAME, FP8, SPARSE, R)                                    \
   __global__ __launch_bounds__(64 * R, 1) void NAME(DecodeArgs a) {              \
     decode_wide<FP8, SPARSE, R>(a);                                              \
   }
 MLA_WIDE_KERNEL(decode_bf16_dense_r4, false, false, 4)
 MLA_WIDE_KERNEL(decode_bf16_dense_r2, false, false, 2)
-MLA_DECODE_KERNEL(decode_bf16_dense_r1, false, false, 1, 2, 1)
+MLA_WIDE_KERNEL(decode_bf16_dense_r1w, false, false, 1)
+MLA_WIDE_KERNEL(decode_bf16_sparse_r1w, false, true, 1)
+MLA_WIDE_KERNEL(decode_fp8_dense_r1w, true, false, 1)
+MLA_WIDE_KERNEL(decode_fp8_sparse_r1w, true, true, 1)
 MLA_WIDE_KERNEL(decode_bf16_sparse_r4, false, true, 4)
 MLA_WIDE_KERNEL(decode_bf16_sparse_r2, false, true, 2)
-MLA_DECODE_KERNEL(decode_bf16_sparse_r1, false, true, 1, 2, 1)
 MLA_WIDE_KERNEL(decode_fp8_dense_r4, true, false, 4)
 MLA_WIDE_KERNEL(decode_fp8_dense_r2, true, false, 2)
-MLA_DECODE_KERNEL(decode_fp8_dense_r1, true, false, 1, 4, 1)
 MLA_WIDE_KERNEL(decode_fp8_sparse_r4, true, true, 4)
 MLA_WIDE_KERNEL(decode_fp8_sparse_r2, true, true, 2)
-MLA_DECODE_KERNEL(decode_fp8_sparse_r1, true, true, 1, 4, 1)
 #undef MLA_WIDE_KERNEL
-#undef MLA_DECODE_KERNEL
 
 // ---------------------------------------------------------------------------
 // Combine: for units with >= 2 splits merge the partial (O/l, log2 lse)
@@ -1563,18 +1051,6 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   if ((threadIdx.x & 127) == 0) a.lse[grow] = (mx + __log2f(wsum)) * kLn2;
 }
 
-template <bool FP8, bool SPARSE, int R, int T, int NBUF>
-hipError_t launch_shape(void (*kern)(DecodeArgs), const Geometry& g, const DecodeArgs& a,
-                        hipStream_t stream) {
-  using S = Shape<FP8, SPARSE, R, T, NBUF>;
-  // Dynamic LDS above 64 KB must be allowed explicitly (cheap, host-side).
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, S::kLdsBytes);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(g.num_wg), dim3(S::kThreads), S::kLdsBytes, stream, a);
-  return hipGetLastError();
-}
-
 template <bool FP8, bool SPARSE, int R>
 hipError_t launch_wide(void (*kern)(DecodeArgs), const Geometry& g, const DecodeArgs& a,
                        hipStream_t stream) {
@@ -1592,21 +1068,21 @@ hipError_t launch_variant(bool fp8, bool sparse, const Geometry& g, const Decode
   if (!fp8 && !sparse) {
     if (shape == 4) return launch_wide<false, false, 4>(decode_bf16_dense_r4, g, a, s);
     if (shape == 2) return launch_wide<false, false, 2>(decode_bf16_dense_r2, g, a, s);
-    return launch_shape<false, false, 1, 2, 1>(decode_bf16_dense_r1, g, a, s);
+    return launch_wide<false, false, 1>(decode_bf16_dense_r1w, g, a, s);
   }
   if (!fp8 && sparse) {
     if (shape == 4) return launch_wide<false, true, 4>(decode_bf16_sparse_r4, g, a, s);
     if (shape == 2) return launch_wide<false, true, 2>(decode_bf16_sparse_r2, g, a, s);
-    return launch_shape<false, true, 1, 2, 1>(decode_bf16_sparse_r1, g, a, s);
+    return launch_wide<false, true, 1>(decode_bf16_sparse_r1w, g, a, s);
   }
   if (!sparse) {
     if (shape == 4) return launch_wide<true, false, 4>(decode_fp8_dense_r4, g, a, s);
     if (shape == 2) return launch_wide<true, false, 2>(decode_fp8_dense_r2, g, a, s);
-    return launch_shape<true, false, 1, 4, 1>(decode_fp8_dense_r1, g, a, s);
+    return launch_wide<true, false, 1>(decode_fp8_dense_r1w, g, a, s);
   }
   if (shape == 4) return launch_wide<true, true, 4>(decode_fp8_sparse_r4, g, a, s);
   if (shape == 2) return launch_wide<true, true, 2>(decode_fp8_sparse_r2, g, a, s);
-  return launch_shape<true, true, 1, 4, 1>(decode_fp8_sparse_r1, g, a, s);
+  return launch_wide<true, true, 1>(decode_fp8_sparse_r1w, g, a, s);
 }
 
 }  // namespace kern

@@ -116,7 +116,7 @@ mla_status mla_plan(const int32_t *cache_seqlens, int B, int Sq, int H, int topk
  *   kv_dtype      MLA_KV_BF16, or MLA_KV_FP8_E4M3 with kv_scales non-NULL
  *   num_pages     pages in kv_pages (>= 1)
  *   bt_stride     int32 entries per block_table row (>= 1)
- *   softmax_scale finite multiplier of the scores (e.g. 1/sqrt(192))
+ *   softmax_scale finite positive multiplier of the scores (e.g. 1/sqrt(192))
  *   causal        nonzero: query s sees tokens j <= L_b - Sq + s
  *   planned       nonzero: mla_plan already filled this workspace
  * Limits: 1 <= Sq*H; sequences with Sq*H > 128 rows are processed as

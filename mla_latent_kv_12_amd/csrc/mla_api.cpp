@@ -115,7 +115,8 @@ mla_status run(const void* q_nope, const void* q_rope, const void* kv_pages, con
   if (B <= 0 || Sq <= 0 || H <= 0) return fail(MLA_ERR_SHAPE, "B, Sq, H must be >= 1 (got %d, %d, %d)", B, Sq, H);
   if (num_pages <= 0 || bt_stride <= 0)
     return fail(MLA_ERR_SHAPE, "num_pages and bt_stride must be >= 1 (got %d, %d)", num_pages, bt_stride);
-  if (!isfinite(softmax_scale)) return fail(MLA_ERR_SHAPE, "softmax_scale must be finite");
+  if (!isfinite(softmax_scale) || !(softmax_scale > 0.f))
+    return fail(MLA_ERR_SHAPE, "softmax_scale must be finite and > 0");
   if (num_wg < 0 || num_wg > kMaxWg) return fail(MLA_ERR_SHAPE, "num_wg out of range [0, %d]", kMaxWg);
   if (!aligned(q_nope, 16) || !aligned(q_rope, 16) || !aligned(kv_pages, 16) || !aligned(out, 16) ||
       (kv_scales && !aligned(kv_scales, 16)) || !aligned(lse, 4) || !aligned(block_table, 4) ||

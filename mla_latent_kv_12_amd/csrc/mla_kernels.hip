@@ -373,8 +373,7 @@ struct Wide {
   static constexpr int kPgOff = kIdxOff + (SPARSE ? kRing * 128 : 0);
   static constexpr int kPOff = kPgOff + (SPARSE ? kRing * 128 : 0);
   static constexpr int kAlphaOff = kPOff + 32 * R * 64;
-  static constexpr int kFlagOff = kAlphaOff + 32 * R * 4;
-  static constexpr int kMrgOff = kFlagOff + 16;
+  static constexpr int kMrgOff = kAlphaOff + 32 * R * 4;
   static constexpr int kDummyOff = kMrgOff + 2 * 32 * R * 4;
   static constexpr int kLdsBytes = kDummyOff + 64;
   static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
@@ -400,7 +399,6 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
   int* const pg_ring = reinterpret_cast<int*>(lds + W::kPgOff);
   uint8_t* const pbuf = lds + W::kPOff;
   float* const alpha_buf = reinterpret_cast<float*>(lds + W::kAlphaOff);
-  int* const flag_buf = reinterpret_cast<int*>(lds + W::kFlagOff);
   float* const mrg = reinterpret_cast<float*>(lds + W::kMrgOff);
   int* const dummy = reinterpret_cast<int*>(lds + W::kDummyOff);
   auto desc = [&](int x) -> int* { return desc_ring + (x & (W::kRing - 1)) * 8; };
@@ -748,7 +746,10 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
 
     // ---- online softmax: lane holds row l32, tokens 8*(i/4) + 4g + i%4.
     // fp8: token scales multiply the scores and, before P.V, the weights.
+    // The row maximum is taken over the unscaled scores (the softmax scale
+    // is positive) and the scale enters each weight's exponent in one FMA.
     const float* scl = reinterpret_cast<const float*>(cur + W::kScaleOff) + 4 * g;
+    const float c2 = a.scale_log2;
     float mloc = kNegInf;
 #pragma unroll
     for (int q4 = 0; q4 < 4; q4++) {
@@ -758,7 +759,7 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
       for (int e = 0; e < 4; e++) {
         const int i = 4 * q4 + e;
         const int tau_rel = 8 * q4 + e;  // token minus 4g
-        float v = sacc[i] * a.scale_log2;
+        float v = sacc[i];
         bool ok;
         if constexpr (!SPARSE) ok = tau_rel + 4 * g < lim;
         else ok = (vm >> tau_rel) & 1u;
@@ -767,13 +768,11 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
         mloc = fmaxf(mloc, sacc[i]);
       }
     }
-    const float mt = pair_max(mloc);
+    const float mt = pair_max(mloc) * c2;  // -inf stays -inf
     const float mnew = fmaxf(m_run, mt);
     const bool need = mnew > m_run + kRescaleSlack;  // -inf + slack = -inf
     const bool moved = __builtin_amdgcn_ballot_w64(need) != 0;
-    // O rows only need scaling if they hold something (m was finite)
-    const bool scale_o = __builtin_amdgcn_ballot_w64(need && m_run != kNegInf) != 0;
-    float alpha = 1.f;
+    float alpha = 1.f;  // exactly 1 unless this row's maximum moved
     if (moved) {
       alpha = (m_run == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m_run - mnew);
       l_run *= alpha;
@@ -789,7 +788,7 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
 #pragma unroll
       for (int e = 0; e < 4; e++) {
         const int i = 4 * q4 + e;
-        float p = __builtin_amdgcn_exp2f(sacc[i] - muse);
+        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], c2, -muse));
         psum += p;
         if constexpr (FP8) p *= (sacc[i] == kNegInf) ? 0.f : sv[e];
         pf[i >> 3][i & 7] = (__bf16)p;
@@ -804,25 +803,22 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
     *reinterpret_cast<bf16x8*>(prow + (((2 * g) ^ pc) << 4)) = pf[0];
     *reinterpret_cast<bf16x8*>(prow + (((2 * g + 1) ^ pc) << 4)) = pf[1];
     if (g == 0) alpha_buf[32 * rg + l32] = alpha;
-    if (lane == 0) flag_buf[rg] = scale_o ? 1 : 0;
     wait_lds();
     barrier();
-    int fl[R];
     float al[R];
+    bool scale_any = false;
 #pragma unroll
     for (int rb = 0; rb < R; rb++) {
-      fl[rb] = flag_buf[rb];
       al[rb] = alpha_buf[32 * rb + l32];
+      scale_any |= al[rb] != 1.f;
     }
-    int fany = 0;
-#pragma unroll
-    for (int rb = 0; rb < R; rb++) fany |= fl[rb];
-    if (__builtin_amdgcn_readfirstlane(fany)) {  // rare: some row's maximum moved
+    // Rare: some row's maximum moved (also the first chunk of a unit, where
+    // alpha is 0 and O still 0).
+    if (__builtin_amdgcn_ballot_w64(scale_any) != 0) {
 #pragma unroll
       for (int rb = 0; rb < R; rb++) {
-        const float f = __builtin_amdgcn_readfirstlane(fl[rb]) ? al[rb] : 1.f;
 #pragma unroll
-        for (int dbl = 0; dbl < DB; dbl++) acc_scale(o[dbl * R + rb], f);
+        for (int dbl = 0; dbl < DB; dbl++) acc_scale(o[dbl * R + rb], al[rb]);
       }
     }
 

@@ -73,6 +73,7 @@ def _decode(**kw):
     (dict(dtype=7), SHAPE), (dict(B=0), SHAPE), (dict(H=-1), SHAPE), (dict(Sq=0), SHAPE),
     (dict(num_pages=0), SHAPE), (dict(bt_stride=0), SHAPE),
     (dict(scale=float("nan")), SHAPE), (dict(scale=float("inf")), SHAPE),
+    (dict(scale=0.0), SHAPE), (dict(scale=-0.1), SHAPE),
     (dict(num_wg=-3), SHAPE), (dict(num_wg=1 << 20), SHAPE),
     (dict(q_nope=FAKE + 8), ALIGN), (dict(kv=FAKE + 4), ALIGN), (dict(out=FAKE + 2), ALIGN),
     (dict(ws=None), WS), (dict(ws=FAKE + 16), ALIGN),

@@ -362,7 +362,7 @@ struct Wide {
   // 4-byte dummy copies), so one wait count serves all of them
   static constexpr int kPerWave = (kNCopy + R - 1) / R;
   static_assert(kNA % R == 0, "region-A copies must split evenly over the waves");
-  static constexpr int kLook = SPARSE ? 2 : 1;      // lookup copies per step (wave 0)
+  static constexpr int kLook = SPARSE ? 2 : 0;      // lookup copies per step (wave 0)
   static constexpr int kLeadDma = kSlots - 1;
   static constexpr int kLeadPage = 2 * kLeadDma;
   static constexpr int kLeadCur = SPARSE ? 3 * kLeadDma : kLeadPage;
@@ -452,24 +452,33 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
   enter();
   if (cu < 0) return;  // uniform: this workgroup has no work
 
-  // Writes the descriptor of the cursor's item x and starts its lookups
-  // (wave 0): the page (dense) or the 32 token positions (sparse).  Always
-  // exactly W::kLook - (SPARSE ? 1 : 0) copies, so the counts stay exact.
+  // Dense chunks are described in scalar registers, compactly: unit, page
+  // (read from the block table by a scalar load, checked at use) and
+  // 2 * (tokens left from the chunk's first token) + half-page.
+  struct DD {
+    int u, pg, remh;
+  };
+  auto cursor_desc = [&]() -> DD {
+    DD d;
+    d.u = cu;
+    d.remh = 2 * (cL - 32 * (2 * ct + ch)) + ch;
+    d.pg = (cu >= 0 && ct < a.bt_stride) ? ldc(a.block_table + (size_t)cs * a.bt_stride + ct) : -1;
+    return d;
+  };
+  // Visible rows at the start of a dense chunk (0 when it has no page).
+  auto dd_nvalid = [&](const DD& d) -> int {
+    const bool ok = d.u >= 0 && d.pg >= 0 && d.pg < a.num_pages;
+    return ok ? min(max(d.remh >> 1, 0), 32) : 0;
+  };
+
+  // Sparse: writes the descriptor of the cursor's item x and starts the
+  // lookups of its 32 token positions (wave 0); always exactly one copy, so
+  // the counts stay exact.
   auto lookup = [&](int x) {
     if (rg != 0) return;
     int* d = desc(x);
     const int th = cu >= 0 ? 2 * ct + ch : -1;
-    if constexpr (!SPARSE) {
-      const bool need = cu >= 0 && ct < a.bt_stride;
-      if (lane == 0) {
-        d[0] = cu;
-        d[1] = th;
-        d[3] = cL;
-        if (!need) d[2] = -1;
-        const int32_t* src = need ? a.block_table + (size_t)cs * a.bt_stride + ct : a.seqlens;
-        copy4_v(src, lds_addr(need ? d + 2 : dummy));
-      }
-    } else {
+    if constexpr (SPARSE) {
       const int b = cs / a.Sq;
       if (lane == 0) {
         d[0] = cu;
@@ -513,16 +522,20 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
     int tok;              // sparse: token (page*64 + row) of row `lane` (< 32), or -1
   };
   // Where item z's rows come from (read from its descriptor and rings).
+  auto source_dense = [&](const DD& d) -> Src {
+    Src r{a.ws_zero, reinterpret_cast<const float*>(a.ws_zero), 0, -1};
+    r.nvalid = dd_nvalid(d);
+    if (r.nvalid > 0) {
+      const int half = d.remh & 1;
+      r.base = a.kv + (size_t)d.pg * (kPage * W::kRowBytes) + half * 32 * W::kRowBytes;
+      r.scales = a.kv_scales + (size_t)d.pg * kPage + half * 32;
+    }
+    return r;
+  };
   auto source = [&](int z, const Desc& dz) -> Src {
     Src r{a.ws_zero, reinterpret_cast<const float*>(a.ws_zero), 0, -1};
-    const int uu = dz.u, th = dz.th, p2 = dz.p2, LL = dz.L;
-    if constexpr (!SPARSE) {
-      if (uu >= 0 && th >= 0 && p2 >= 0 && p2 < a.num_pages) {
-        r.nvalid = min(max(LL - 32 * th, 0), 32);
-        r.base = a.kv + (size_t)p2 * (kPage * W::kRowBytes) + (th & 1) * 32 * W::kRowBytes;
-        r.scales = a.kv_scales + (size_t)p2 * kPage + (th & 1) * 32;
-      }
-    } else {
+    const int uu = dz.u, th = dz.th, LL = dz.L;
+    {
       const int ri = z & (W::kRing - 1);
       const int idx = lane < 32 ? idx_ring[ri * 32 + lane] : -1;
       const int pg = lane < 32 ? pg_ring[ri * 32 + lane] : -1;
@@ -588,8 +601,7 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
       }
     }
   };
-  auto copy_all = [&](int z) {
-    const Src sr = source(z, read_desc(z));
+  auto copy_all = [&](int z, const Src& sr) {
     const uint32_t slot = lds_addr(slots + (z % W::kSlots) * W::kSlotBytes);
 #pragma unroll
     for (int j = 0; j < W::kPerWave; j++) copy(j, slot, sr);
@@ -653,39 +665,19 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
   const int G16 = lane >> 4, i16 = lane & 15;
   const int ya = g ^ (FP8 ? 0 : sw16(l32));  // bf16 region A (score operand)
   const int yb = g ^ ((l32 >> 1) & 7);       // bf16 region B
-  int vbase = 0, vy0 = 0, vy1 = 0;
-  int voff8[4] = {0, 0, 0, 0};
-  if constexpr (!FP8) {
-    // transposed reads: lane loads token 16ks + 8r + 4(G16>>1) + (i16>>2),
-    // dims 32db + 16(G16&1) + 4(i16&3) .. +3
-    vbase = (4 * (G16 >> 1) + (i16 >> 2)) * 1024 + 8 * (i16 & 1);
-    const int w = 2 * (G16 & 1) + ((i16 >> 1) & 1);
-    vy0 = w ^ (((i16 >> 2) << 2) | ((G16 >> 1) & 3));
-    vy1 = w ^ (((i16 >> 2) << 2) | ((2 + (G16 >> 1)) & 3));
-  } else {
-    // fp8: lane loads token 16ks + 8(i16>>3) + z8, bytes 32db + 16(G16&1) + 8(i16&1) .. +7
-    const int z8 = 4 * (G16 >> 1) + ((i16 >> 1) & 3);
-    const int trow = 8 * (i16 >> 3) + z8;
-#pragma unroll
-    for (int p4 = 0; p4 < 4; p4++) voff8[p4] = trow * 512 + (((2 * p4 + (G16 & 1)) ^ z8) << 4) + 8 * (i16 & 1);
-  }
-
   // ------------------------------------------------------------ one step
   // Computes item s (in `cur`) and issues this wave's copies of item z into
   // `nxt` between the score MFMAs.
-  auto step = [&](const uint8_t* __restrict__ cur, uint32_t nxt, const Src& sr, int s,
-                  const Desc& dc, const UnitInfo& ui) {
-    const int th = dc.th;
+  auto step = [&](const uint8_t* __restrict__ cur, uint32_t nxt, const Src& sr, int s, int nv,
+                  int rem, const UnitInfo& ui) {
+    // dense: nv visible rows at the chunk's start, rem = length - first token
     int lim = 0;
     unsigned vm = 0;
     if constexpr (!SPARSE) {
-      const int p2 = dc.p2;
-      const int LL = dc.L;
-      const int nvalid = (th >= 0 && p2 >= 0 && p2 < a.num_pages) ? min(max(LL - 32 * th, 0), 32) : 0;
-      lim = nvalid;
+      lim = nv;
       if (a.causal) {
         const int srow = (ui.rin_b0 + rg * kRowsPerWave + l32) / a.H;
-        lim = min(lim, LL - a.Sq + srow + 1 - 32 * th);
+        lim = min(lim, rem - a.Sq + srow + 1);
       }
     } else {
       vm = (unsigned)__builtin_amdgcn_readfirstlane(desc(s)[4]) >> (4 * g);
@@ -700,7 +692,10 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
     f32x16 sacc = {};
     constexpr int kLead = 6, kRingK = 8;
     const uint32_t cur_a = lds_addr(cur);
-    wait_lds();  // nothing else outstanding: the counts below are exact
+    // Dense: no wait here.  A scalar load still in flight (the block table)
+    // only makes the counted waits below stricter, never looser, since LDS
+    // operations complete in order.
+    if constexpr (SPARSE) wait_lds();
     if constexpr (!FP8) {
       uint32_t adA[8], adB[4];
 #pragma unroll
@@ -822,6 +817,29 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
       }
     }
 
+    // Lane offsets of the transposed V reads, recomputed here from a
+    // laundered lane index so that they are not held (beside Q) through the
+    // score loop, where registers are scarcest.
+    int lnv = lane;
+    asm volatile("" : "+v"(lnv));
+    const int G16v = lnv >> 4, i16v = lnv & 15;
+    int vbase = 0, vy0 = 0, vy1 = 0;
+    int voff8[4] = {0, 0, 0, 0};
+    if constexpr (!FP8) {
+      // transposed reads: lane loads token 16ks + 8r + 4(G16v>>1) + (i16v>>2),
+      // dims 32db + 16(G16v&1) + 4(i16v&3) .. +3
+      vbase = (4 * (G16v >> 1) + (i16v >> 2)) * 1024 + 8 * (i16v & 1);
+      const int w = 2 * (G16v & 1) + ((i16v >> 1) & 1);
+      vy0 = w ^ (((i16v >> 2) << 2) | ((G16v >> 1) & 3));
+      vy1 = w ^ (((i16v >> 2) << 2) | ((2 + (G16v >> 1)) & 3));
+    } else {
+      // fp8: lane loads token 16ks + 8(i16v>>3) + z8, bytes 32db + 16(G16v&1) + 8(i16v&1) .. +7
+      const int z8 = 4 * (G16v >> 1) + ((i16v >> 1) & 3);
+      const int trow = 8 * (i16v >> 3) + z8;
+#pragma unroll
+      for (int p4 = 0; p4 < 4; p4++) voff8[p4] = trow * 512 + (((2 * p4 + (G16v & 1)) ^ z8) << 4) + 8 * (i16v & 1);
+    }
+
     // ---- O^T[dim][row] += V^T[dim][token] . P^T[token][row]; k-step kk
     // covers tokens 16kk..16kk+15 in the accumulator order of S^T.
     auto vload = [&](int kk, int db) -> bf16x8 {
@@ -916,25 +934,37 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
   };
 
   // ------------------------------------------------------------ prologue
-#pragma unroll 1
-  for (int x = 0; x < W::kLeadCur; x++) {
-    lookup(x);
-    next();
-  }
-  wait_vm<0>();
-  wait_lds();
-  barrier();
+  // Dense: fq[i] describes item s + i; the last entry's page load is the
+  // one in flight.
+  constexpr int kQ = W::kLeadDma + 2;
+  DD fq[kQ];
   if constexpr (SPARSE) {
+#pragma unroll 1
+    for (int x = 0; x < W::kLeadCur; x++) {
+      lookup(x);
+      next();
+    }
+    wait_vm<0>();
+    wait_lds();
+    barrier();
 #pragma unroll 1
     for (int y = 0; y < W::kLeadPage; y++) page_lookup(y);
     wait_vm<0>();
     wait_lds();
     barrier();
-  }
 #pragma unroll 1
-  for (int z = 0; z < W::kLeadDma; z++) {
-    dummy_lookups();
-    copy_all(z);
+    for (int z = 0; z < W::kLeadDma; z++) {
+      dummy_lookups();
+      copy_all(z, source(z, read_desc(z)));
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kQ; i++) {
+      fq[i] = cursor_desc();
+      next();
+    }
+#pragma unroll
+    for (int z = 0; z < W::kLeadDma; z++) copy_all(z, source_dense(fq[z]));
   }
 
   // ------------------------------------------------------------ main loop
@@ -945,8 +975,13 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
   wait_item();
   wait_lds();
   barrier();
-  Desc dc = read_desc(0);
-  Desc dz = read_desc(W::kLeadDma);
+  Desc dc{}, dz{};
+  if constexpr (SPARSE) {
+    dc = read_desc(0);
+    dz = read_desc(W::kLeadDma);
+  } else {
+    dc.u = fq[0].u;
+  }
   int uu = dc.u;
   UnitInfo ui{};
   if (uu >= 0) {
@@ -959,19 +994,35 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
     reset();
 #pragma unroll 1
     do {
-      lookup(s + W::kLeadCur);
-      next();
-      page_lookup(s + W::kLeadPage);
       const int z = s + W::kLeadDma;
-      const Src sr = source(z, dz);
+      Src sr;
+      int nv = 0, rem = 0;
+      if constexpr (SPARSE) {
+        lookup(s + W::kLeadCur);
+        next();
+        page_lookup(s + W::kLeadPage);
+        sr = source(z, dz);
+      } else {
+        sr = source_dense(fq[W::kLeadDma]);
+        nv = dd_nvalid(fq[0]);
+        rem = fq[0].remh >> 1;
+      }
       step(slots + (s % W::kSlots) * W::kSlotBytes, lds_addr(slots + (z % W::kSlots) * W::kSlotBytes),
-           sr, s, dc, ui);
+           sr, s, nv, rem, ui);
       s++;
       wait_item();
       wait_lds();
       barrier();  // item s is in LDS for every wave; step s-1 is done everywhere
-      dc = read_desc(s);
-      dz = read_desc(s + W::kLeadDma);
+      if constexpr (SPARSE) {
+        dc = read_desc(s);
+        dz = read_desc(s + W::kLeadDma);
+      } else {
+#pragma unroll
+        for (int i = 0; i + 1 < kQ; i++) fq[i] = fq[i + 1];
+        fq[kQ - 1] = cursor_desc();  // its page load completes during the next step
+        next();
+        dc.u = fq[0].u;
+      }
     } while (dc.u == uu);
     const UnitInfo done = ui;
     if (dc.u >= 0) {

@@ -90,7 +90,7 @@ typedef enum { MLA_KV_BF16 = 0, MLA_KV_FP8_E4M3 = 1 } mla_kv_dtype;
  * Bytes of device workspace a call with these sizes needs (0 on invalid
  * sizes).  topk = 0 selects the dense path, topk > 0 the sparse path.
  * num_wg is the number of persistent workgroups the work is spread over;
- * 0 means one per compute unit of the current device, or two per compute
+ * 0 means one per compute unit of the current device, or four per compute
  * unit when a scheduling unit has at most 32 query rows (Sq*H <= 32 dense,
  * H <= 32 sparse), whose one-wave workgroups share a unit.  The same
  * (B, Sq, H, topk, num_wg) must be passed to mla_plan / mla_decode /

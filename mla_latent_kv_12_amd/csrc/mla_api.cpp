@@ -65,13 +65,13 @@ bool make_geometry(int B, int Sq, int H, int topk, int num_wg, mla::Geometry* g)
   return true;
 }
 
-// Workgroup count: the caller's, or one per compute unit (two for units of
-// at most 32 query rows, whose one-wave workgroups fit two to a unit).
+// Workgroup count: the caller's, or one per compute unit (four for units of
+// at most 32 query rows, whose one-wave workgroups share a unit).
 int resolve_wg(int num_wg, int Sq, int H, int topk) {
   if (num_wg > 0) return num_wg;
   const long long rows = topk > 0 ? (long long)H : (long long)Sq * H;
   const int cus = device_cus();
-  return rows <= 32 ? 2 * cus : cus;
+  return rows <= 32 ? 4 * cus : cus;
 }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }

@@ -22,7 +22,7 @@
 // Wave roles: the R waves of a workgroup (R = 4, 2, 1 for units of up to
 // 128, 64, 32 query rows) share each chunk in LDS.  For the scores a wave
 // owns 32 query rows; for P.V it owns 512/R output dims of all the unit's
-// rows.  One-wave workgroups run two to a compute unit.
+// rows.  One-wave workgroups run four (fp8) or two (bf16) to a compute unit.
 #include "mla_internal.h"
 
 #include <utility>
@@ -352,9 +352,9 @@ struct Wide {
   static constexpr int kRegB = kRows * kABytes;     // region B (RoPE part) offset
   static constexpr int kScaleOff = kRegB + kRows * kDR * kEB;
   static constexpr int kSlotBytes = kScaleOff + (FP8 ? 128 : 0);
-  // Two workgroups of one wave share a compute unit for units of <= 32 rows,
-  // so a bf16 one-wave workgroup keeps two chunks in flight instead of four.
-  static constexpr int kSlots = (R == 1 && !FP8) ? 2 : 4;
+  // One-wave workgroups (units of <= 32 rows) run four to a compute unit
+  // (fp8; bf16 slots fit two) and keep two chunks in LDS.
+  static constexpr int kSlots = (R == 1) ? 2 : 4;
   static constexpr int kNA = FP8 ? 16 : 32;         // 1 KB copies of region A
   static constexpr int kNB = FP8 ? 2 : 4;           // 1 KB copies of region B
   static constexpr int kNCopy = kNA + kNB + (FP8 ? 1 : 0);  // (+ the 32 scales)

@@ -662,7 +662,6 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
   };
 
   // Per-lane pieces of the swizzled LDS addresses.
-  const int G16 = lane >> 4, i16 = lane & 15;
   const int ya = g ^ (FP8 ? 0 : sw16(l32));  // bf16 region A (score operand)
   const int yb = g ^ ((l32 >> 1) & 7);       // bf16 region B
   // ------------------------------------------------------------ one step
@@ -1073,23 +1072,41 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   if (r >= ui.rows) return;
   const size_t grow = (size_t)ui.row0 + r;
   uint16_t* dst = a.out + grow * kDC + d4;
-  float mx = kNegInf;
+  // One pass with a running maximum; the partials are loaded four splits at
+  // a time so that several loads are in flight per thread.
   const int base = a.ws_meta[4 * uu + 1];
-  for (int i = 0; i < ns; i++) mx = fmaxf(mx, a.ws_plse[(size_t)(base + i) * kMaxUnitRows + r]);
+  float mx = kNegInf, wsum = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  auto merge = [&](float li, const f32x4& v) {
+    const float mn = fmaxf(mx, li);
+    if (mn == kNegInf) return;  // nothing seen yet
+    const float sc = __builtin_amdgcn_exp2f(mx - mn);  // 0 while mx is -inf
+    const float w = __builtin_amdgcn_exp2f(li - mn);   // 0 for an empty split
+    acc = acc * sc + w * v;
+    wsum = wsum * sc + w;
+    mx = mn;
+  };
+  int i = 0;
+  for (; i + 4 <= ns; i += 4) {
+    float l4[4];
+    f32x4 v4[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const size_t sp = (size_t)(base + i + j) * kMaxUnitRows + r;
+      l4[j] = a.ws_plse[sp];
+      v4[j] = *reinterpret_cast<const f32x4*>(a.ws_po + sp * kDC + d4);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; j++) merge(l4[j], v4[j]);
+  }
+  for (; i < ns; i++) {
+    const size_t sp = (size_t)(base + i) * kMaxUnitRows + r;
+    merge(a.ws_plse[sp], *reinterpret_cast<const f32x4*>(a.ws_po + sp * kDC + d4));
+  }
   if (ns == 0 || mx == kNegInf) {
     *reinterpret_cast<u32x2*>(dst) = u32x2{0u, 0u};
     if ((threadIdx.x & 127) == 0) a.lse[grow] = kNegInf;
     return;
-  }
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  float wsum = 0.f;
-  for (int i = 0; i < ns; i++) {
-    const size_t sp = (size_t)(base + i) * kMaxUnitRows + r;
-    const float li = a.ws_plse[sp];
-    const float w = (li == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(li - mx);
-    wsum += w;
-    const f32x4 v = *reinterpret_cast<const f32x4*>(a.ws_po + sp * kDC + d4);
-    acc += w * v;
   }
   const float inv = 1.0f / wsum;
   bf16x2 p0 = {(__bf16)(acc[0] * inv), (__bf16)(acc[1] * inv)};

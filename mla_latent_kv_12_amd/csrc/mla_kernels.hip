@@ -415,15 +415,15 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
   // The lookup cursor walks the workgroup's chunks: unit cu (-1 once done),
   // tile ct, half ch, tile range end chi, sequence (dense b / sparse su) cs
   // and its length cL.  Every wave runs it (uniform scalar code).
-  const int u_end = a.ws_work[2 * wg + 2], t_end = a.ws_work[2 * wg + 3];
-  int cu = a.ws_work[2 * wg], ct = a.ws_work[2 * wg + 1], ch = 0, chi = 0, cs = 0, cL = 0;
+  const int u_end = ldc(a.ws_work + 2 * wg + 2), t_end = ldc(a.ws_work + 2 * wg + 3);
+  int cu = ldc(a.ws_work + 2 * wg), ct = ldc(a.ws_work + 2 * wg + 1), ch = 0, chi = 0, cs = 0, cL = 0;
   auto enter = [&]() {  // settle (cu, ct) on the next unit with a chunk left
     for (;;) {
       if (cu > u_end || cu >= a.n_units) {
         cu = -1;
         return;
       }
-      chi = (cu == u_end) ? t_end : a.ws_meta[4 * cu];
+      chi = (cu == u_end) ? t_end : ldc(a.ws_meta + 4 * cu);
       if (ct < chi) break;
       cu++;
       ct = 0;
@@ -431,7 +431,7 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
     ch = 0;
     cs = cu / a.row_blocks;
     const int b = SPARSE ? cs / a.Sq : cs;
-    cL = max(a.seqlens[b], 0);
+    cL = max(ldc(a.seqlens + b), 0);
   };
   auto next = [&]() {
     if (cu < 0) return;
@@ -536,14 +536,16 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
     Src r{a.ws_zero, reinterpret_cast<const float*>(a.ws_zero), 0, -1};
     const int uu = dz.u, th = dz.th, LL = dz.L;
     {
+      int ln = lane;
+      asm volatile("" : "+v"(ln));  // recomputed here, not kept live across the loop
       const int ri = z & (W::kRing - 1);
-      const int idx = lane < 32 ? idx_ring[ri * 32 + lane] : -1;
-      const int pg = lane < 32 ? pg_ring[ri * 32 + lane] : -1;
+      const int idx = ln < 32 ? idx_ring[ri * 32 + ln] : -1;
+      const int pg = ln < 32 ? pg_ring[ri * 32 + ln] : -1;
       const bool ok = uu >= 0 && th >= 0 && idx >= 0 && idx < LL && (idx >> 6) < a.bt_stride &&
                       pg >= 0 && pg < a.num_pages;
       r.tok = ok ? pg * kPage + (idx & 63) : -1;
       const unsigned m = (unsigned)__builtin_amdgcn_ballot_w64(ok);
-      if (rg == 0 && lane == 0) desc(z)[4] = (int)m;
+      if (rg == 0 && ln == 0) desc(z)[4] = (int)m;
     }
     return r;
   };

@@ -770,7 +770,8 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
     const bool moved = __builtin_amdgcn_ballot_w64(need) != 0;
     float alpha = 1.f;  // exactly 1 unless this row's maximum moved
     if (moved) {
-      alpha = (m_run == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m_run - mnew);
+      // A row with no finite score yet has O = 0 and l = 0: nothing to scale.
+      alpha = (m_run == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run - mnew);
       l_run *= alpha;
       m_run = mnew;
     }
@@ -808,8 +809,7 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
       al[rb] = alpha_buf[32 * rb + l32];
       scale_any |= al[rb] != 1.f;
     }
-    // Rare: some row's maximum moved (also the first chunk of a unit, where
-    // alpha is 0 and O still 0).
+    // Rare: some row's maximum moved after it had seen a finite score.
     if (__builtin_amdgcn_ballot_w64(scale_any) != 0) {
 #pragma unroll
       for (int rb = 0; rb < R; rb++) {

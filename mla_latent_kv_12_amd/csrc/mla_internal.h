@@ -18,9 +18,11 @@ constexpr int kBytesFp8Row = kD;        // 576
 constexpr int kTileBf16 = kPage * kBytesBf16Row;  // 73728
 constexpr int kTileFp8 = kPage * kBytesFp8Row;    // 36864
 
-// Scheduling constants: a split costs this many tiles of fixed work (query
-// load + partial write/read), and a workgroup is never given less work.
-constexpr int kSplitCost = 2;
+// Scheduling constants: a split costs this many tiles of fixed work (its
+// query load and its partial written and read back: ~660 KB at 128 rows,
+// nine 72 KB tiles' worth of bytes; 6 measured best), and a workgroup is
+// never given less work.
+constexpr int kSplitCost = 6;
 constexpr int kMinWgCost = 2;
 
 // Problem geometry after the host has folded (B, Sq, H, sparse) into units.

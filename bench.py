@@ -190,7 +190,7 @@ def main():
         roof = {"bound": "mfma", "achieved": round(a_tf, 2), "peak": MFMA_BF16_PEAK_TFS,
                 "unit": "TFLOP/s", "frac": round(a_tf / MFMA_BF16_PEAK_TFS, 4)}
     roof["traffic"] = measured_traffic(args.workload)
-    roof["kernel"] = "mla_attend (decode_*_r4/r2/r1)"
+    roof["kernel"] = "mla_attend (decode_*_r4 / r2 / r1w)"
     roof["kernel_ms"] = round(attend_ms, 5)
     roof["mfma_frac"] = round(flop / (attend_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS, 4)
 

@@ -917,7 +917,9 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
         }
         if (lse_writer) a.lse[(size_t)ui.row0 + r] = empty ? kNegInf : lse2 * kLn2;
       } else {
-        float* dst = a.ws_po + ((size_t)split * kMaxUnitRows + r) * kDC + 4 * g;
+        // Partials are stored in fragment order (see combine_kernel): each
+        // store writes 1 KB of consecutive bytes, one 16-byte piece per lane.
+        float* dst = a.ws_po + (size_t)split * (kMaxUnitRows * kDC) + 4 * ln;
 #pragma unroll
         for (int dbl = 0; dbl < DB; dbl++) {
           const int db = DB * rg + dbl;
@@ -926,7 +928,7 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
           for (int q = 0; q < 4; q++) {
             f32x4 w = {acc_get(ob, 4 * q) * inv, acc_get(ob, 4 * q + 1) * inv,
                        acc_get(ob, 4 * q + 2) * inv, acc_get(ob, 4 * q + 3) * inv};
-            *reinterpret_cast<f32x4*>(dst + 32 * db + 8 * q) = w;
+            *reinterpret_cast<f32x4*>(dst + 256 * ((rb * 16 + db) * 4 + q)) = w;
           }
         }
         if (lse_writer) a.ws_plse[(size_t)split * kMaxUnitRows + r] = lse2;
@@ -1061,22 +1063,32 @@ MLA_WIDE_KERNEL(decode_fp8_sparse_r2, true, true, 2)
 // ---------------------------------------------------------------------------
 // Combine: for units with >= 2 splits merge the partial (O/l, log2 lse)
 // results; units with no tokens at all get out = 0, lse = -inf.
-// Block = 256 threads = 2 rows x 128 threads x 4 dims.
+//
+// Partial layout per split: 256 blocks of 1 KB in fragment order.  Block
+// (rb, db, q) = (rb * 16 + db) * 4 + q holds, at lane L = 32 g + l (16 bytes
+// each), row 32 rb + l, dims 32 db + 8 q + 4 g .. +3: the order in which a
+// wave's accumulators leave the registers.  Each 64-thread group of a block
+// merges one fragment block: thread L handles row 32 rb + l, 4 dims.
 // ---------------------------------------------------------------------------
 template <bool SPARSE>
 __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   const int uu = blockIdx.x;
   const int ns = a.ws_meta[4 * uu + 2];
   if (ns == 1) return;
-  const int half = threadIdx.x >> 7, d4 = (threadIdx.x & 127) * 4;
-  const int r = blockIdx.y * 2 + half;
+  const int blk = blockIdx.y * 4 + (threadIdx.x >> 6);
+  const int ln = threadIdx.x & 63;
+  const int q = blk & 3, db = (blk >> 2) & 15, rb = blk >> 6;
+  const int r = 32 * rb + (ln & 31);
   UnitInfo ui = unit_info(a, SPARSE, uu);
   if (r >= ui.rows) return;
+  const int d4 = 32 * db + 8 * q + 4 * (ln >> 5);
   const size_t grow = (size_t)ui.row0 + r;
   uint16_t* dst = a.out + grow * kDC + d4;
+  const bool lse_writer = db == 0 && q == 0 && ln < 32;
   // One pass with a running maximum; the partials are loaded four splits at
   // a time so that several loads are in flight per thread.
   const int base = a.ws_meta[4 * uu + 1];
+  const size_t frag = (size_t)blk * 256 + 4 * ln;
   float mx = kNegInf, wsum = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   auto merge = [&](float li, const f32x4& v) {
@@ -1094,27 +1106,28 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
     f32x4 v4[4];
 #pragma unroll
     for (int j = 0; j < 4; j++) {
-      const size_t sp = (size_t)(base + i + j) * kMaxUnitRows + r;
-      l4[j] = a.ws_plse[sp];
-      v4[j] = *reinterpret_cast<const f32x4*>(a.ws_po + sp * kDC + d4);
+      const size_t sp = (size_t)(base + i + j);
+      l4[j] = a.ws_plse[sp * kMaxUnitRows + r];
+      v4[j] = *reinterpret_cast<const f32x4*>(a.ws_po + sp * (kMaxUnitRows * kDC) + frag);
     }
 #pragma unroll
     for (int j = 0; j < 4; j++) merge(l4[j], v4[j]);
   }
   for (; i < ns; i++) {
-    const size_t sp = (size_t)(base + i) * kMaxUnitRows + r;
-    merge(a.ws_plse[sp], *reinterpret_cast<const f32x4*>(a.ws_po + sp * kDC + d4));
+    const size_t sp = (size_t)(base + i);
+    merge(a.ws_plse[sp * kMaxUnitRows + r],
+          *reinterpret_cast<const f32x4*>(a.ws_po + sp * (kMaxUnitRows * kDC) + frag));
   }
   if (ns == 0 || mx == kNegInf) {
     *reinterpret_cast<u32x2*>(dst) = u32x2{0u, 0u};
-    if ((threadIdx.x & 127) == 0) a.lse[grow] = kNegInf;
+    if (lse_writer) a.lse[grow] = kNegInf;
     return;
   }
   const float inv = 1.0f / wsum;
   bf16x2 p0 = {(__bf16)(acc[0] * inv), (__bf16)(acc[1] * inv)};
   bf16x2 p1 = {(__bf16)(acc[2] * inv), (__bf16)(acc[3] * inv)};
   *reinterpret_cast<u32x2*>(dst) = u32x2{__builtin_bit_cast(unsigned, p0), __builtin_bit_cast(unsigned, p1)};
-  if ((threadIdx.x & 127) == 0) a.lse[grow] = (mx + __log2f(wsum)) * kLn2;
+  if (lse_writer) a.lse[grow] = (mx + __log2f(wsum)) * kLn2;
 }
 
 template <bool FP8, bool SPARSE, int R>
@@ -1188,7 +1201,7 @@ hipError_t launch_decode(const Geometry& g, const DecodeArgs& a, bool fp8, hipSt
 }
 
 hipError_t launch_combine(const Geometry& g, const DecodeArgs& a, hipStream_t stream) {
-  dim3 grid(g.n_units, (g.m_unit + 1) / 2);
+  dim3 grid(g.n_units, ((g.m_unit + 31) / 32) * 16);  // 4 fragment blocks of 1 KB per block
   if (g.sparse)
     hipLaunchKernelGGL(combine_kernel<true>, grid, dim3(256), 0, stream, a);
   else

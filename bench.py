@@ -4,7 +4,10 @@ One step = one full decode of the workload through the C ABI: the split-KV
 scheduling pass (mla_plan), the main pass (mla_attend) and the split merge
 (mla_combine), over inputs already resident in HBM.  Steps rotate over
 several copies of the latent cache so consecutive steps do not find it in
-the 256 MB last-level cache.
+the 256 MB last-level cache.  `--graph` times replays of the three calls
+captured as one HIP graph per cache copy instead of plain stream launches
+(the calls never allocate or synchronise, so they capture as they are; on
+MI355X this measured the same step time).
 
 Prints one JSON line.  `value` is algorithmic TFLOP/s of the whole step;
 `roofline` describes the main kernel (mla_attend) timed with HIP events on
@@ -117,6 +120,7 @@ def main():
     ap.add_argument("--copies", type=int, default=3, help="cache copies rotated over steps")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true", help="time HIP graph replays of the step")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run plain 1 GiB device copies (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -174,9 +178,28 @@ def main():
         step(k, evs[k])
     t_end.record()
     torch.cuda.synchronize()
-    ms = t_start.elapsed_time(t_end) / args.steps
+    ms_eager = t_start.elapsed_time(t_end) / args.steps
     attend_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
     assert torch.isfinite(lse).all(), "non-finite lse"
+    ms = ms_eager
+    if args.graph:
+        # One graph per cache copy; replayed in the same rotation.
+        graphs = []
+        for i in range(args.copies):
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                step(i)
+            graphs.append(gr)
+        for k in range(args.warmup):
+            graphs[k % args.copies].replay()
+        torch.cuda.synchronize()
+        t_start.record()
+        for k in range(args.steps):
+            graphs[k % args.copies].replay()
+        t_end.record()
+        torch.cuda.synchronize()
+        ms = t_start.elapsed_time(t_end) / args.steps
+        assert torch.isfinite(lse).all(), "non-finite lse"
 
     tflops = flop / (ms * 1e-3) / 1e12
     achieved_gbs = nbytes / (attend_ms * 1e-3) / 1e9
@@ -202,7 +225,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "B": B, "Sq": Sq, "H": H,
                    "tokens": int(inp["cache_seqlens"].sum()), "kv": inp["kv_dtype"],
-                   "topk": topk, "seed": inp["seed"], "cache_copies": args.copies},
+                   "topk": topk, "seed": inp["seed"], "cache_copies": args.copies,
+                   "launch": "hip_graph" if args.graph else "stream"},
+        "ms_per_step_stream_launch": round(ms_eager, 5),
         "gbps_step": round(nbytes / (ms * 1e-3) / 1e9, 1),
         "alg_bytes": nbytes, "alg_flop": flop,
         "roofline": roof,

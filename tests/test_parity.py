@@ -151,6 +151,45 @@ def test_plan_once_then_planned_calls():
     check(out1, lse1, ref[0], ref[1], "planned")
 
 
+@pytest.mark.parametrize("name", ["dsv3_decode", "fp8_head_slice", "dsa_sparse"])
+def test_graph_replay_matches_eager(name):
+    """The three calls (plan, main pass, combine) captured into one HIP graph:
+    every replay, with other eager work and synchronisations in between,
+    gives exactly the eager result (the calls enqueue no memsets)."""
+    inp = S.make_inputs(S.shrink(name), unselected="nan")
+    g = dev(inp)
+    m = mla()
+    B, Sq, H, topk = inp["B"], inp["Sq"], inp["H"], inp["topk"]
+    ws = m.alloc_workspace(B, Sq, H, topk)
+    out = torch.empty((B, Sq, H, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, Sq, H), dtype=torch.float32, device="cuda")
+
+    def calls():
+        m.plan(g["cache_seqlens"], B, Sq, H, ws, topk=topk)
+        m.attend(g["q_nope"], g["q_rope"], g["kv_pages"], g["block_table"], g["cache_seqlens"],
+                 g["softmax_scale"], ws, kv_scales=g["kv_scales"], indices=g["indices"],
+                 causal=g["causal"], out=out, lse=lse)
+        m.combine(g["cache_seqlens"], B, Sq, H, out, lse, ws, topk=topk)
+
+    calls()
+    torch.cuda.synchronize()
+    ref_out, ref_lse = out.clone(), lse.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        calls()
+    for rep in range(3):
+        out.fill_(7.0)
+        lse.fill_(7.0)
+        other = run(g)  # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse), f"replay {rep} differs"
+        assert torch.equal(other[0], ref_out)
+    ref = oracle.decode(inp)
+    check(out, lse, ref[0], ref[1], name + " graph replay")
+
+
 def test_out_of_range_block_table_entries_are_skipped():
     inp = custom(B=2, H=32, lens=(300, 200), seed=4)
     bad = dict(inp)

@@ -237,46 +237,42 @@ __device__ __forceinline__ int xcd_logical(int i, int G) {
 // them itself (s_waitcnt vmcnt with the exact number of younger copies), so
 // the compiler must neither wait for them on its own nor move them across
 // the explicit waits.  Each copy points M0 at the LDS destination (every
-// active lane writes M0 + 4*lane words of its size) and restores M0.
+// active lane writes M0 + 4*lane words of its size).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)reinterpret_cast<uintptr_t>(p);
 }
 // 16 bytes per lane from a wave-uniform base plus a per-lane byte offset.
+// M0 is declared clobbered, so the compiler restores it itself wherever it
+// relies on it.
 __device__ __forceinline__ void copy16_s(const void* base, uint32_t voff, uint32_t lds) {
-  uint32_t keep;
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
+      "s_mov_b32 m0, %2\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %2\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(keep)
-      : "v"(voff), "s"(base), "s"(lds));
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(voff), "s"(base), "s"(lds)
+      : "m0");
 }
 // 16 bytes per lane from a per-lane address.
 __device__ __forceinline__ void copy16_v(const void* addr, uint32_t lds) {
-  uint32_t keep;
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
+      "s_mov_b32 m0, %1\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(keep)
-      : "v"(addr), "s"(lds));
+      "global_load_lds_dwordx4 %0, off"
+      :
+      : "v"(addr), "s"(lds)
+      : "m0");
 }
 // 4 bytes per lane from a per-lane address.
 __device__ __forceinline__ void copy4_v(const void* addr, uint32_t lds) {
-  uint32_t keep;
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
+      "s_mov_b32 m0, %1\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dword %1, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(keep)
-      : "v"(addr), "s"(lds));
+      "global_load_lds_dword %0, off"
+      :
+      : "v"(addr), "s"(lds)
+      : "m0");
 }
 template <int N>
 __device__ __forceinline__ void wait_vm() {
@@ -1000,12 +996,18 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
       const int z = s + W::kLeadDma;
       Src sr;
       int nv = 0, rem = 0;
+      DD nd{};
       if constexpr (SPARSE) {
         lookup(s + W::kLeadCur);
         next();
         page_lookup(s + W::kLeadPage);
         sr = source(z, dz);
       } else {
+        // Item s + kQ enters the queue at the end of this step.  Its block
+        // table entry is requested here, a whole step before the queue
+        // shift copies it (the copy waits for the scalar load to land).
+        nd = cursor_desc();
+        next();
         sr = source_dense(fq[W::kLeadDma]);
         nv = dd_nvalid(fq[0]);
         rem = fq[0].remh >> 1;
@@ -1022,8 +1024,7 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
       } else {
 #pragma unroll
         for (int i = 0; i + 1 < kQ; i++) fq[i] = fq[i + 1];
-        fq[kQ - 1] = cursor_desc();  // its page load completes during the next step
-        next();
+        fq[kQ - 1] = nd;
         dc.u = fq[0].u;
       }
     } while (dc.u == uu);

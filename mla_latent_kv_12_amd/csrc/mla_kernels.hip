@@ -237,42 +237,46 @@ __device__ __forceinline__ int xcd_logical(int i, int G) {
 // them itself (s_waitcnt vmcnt with the exact number of younger copies), so
 // the compiler must neither wait for them on its own nor move them across
 // the explicit waits.  Each copy points M0 at the LDS destination (every
-// active lane writes M0 + 4*lane words of its size).
+// active lane writes M0 + 4*lane words of its size) and restores M0.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)reinterpret_cast<uintptr_t>(p);
 }
 // 16 bytes per lane from a wave-uniform base plus a per-lane byte offset.
-// M0 is declared clobbered, so the compiler restores it itself wherever it
-// relies on it.
 __device__ __forceinline__ void copy16_s(const void* base, uint32_t voff, uint32_t lds) {
+  uint32_t keep;
   asm volatile(
-      "s_mov_b32 m0, %2\n\t"
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, %1"
-      :
-      : "v"(voff), "s"(base), "s"(lds)
-      : "m0");
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(keep)
+      : "v"(voff), "s"(base), "s"(lds));
 }
 // 16 bytes per lane from a per-lane address.
 __device__ __forceinline__ void copy16_v(const void* addr, uint32_t lds) {
+  uint32_t keep;
   asm volatile(
-      "s_mov_b32 m0, %1\n\t"
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, off"
-      :
-      : "v"(addr), "s"(lds)
-      : "m0");
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(keep)
+      : "v"(addr), "s"(lds));
 }
 // 4 bytes per lane from a per-lane address.
 __device__ __forceinline__ void copy4_v(const void* addr, uint32_t lds) {
+  uint32_t keep;
   asm volatile(
-      "s_mov_b32 m0, %1\n\t"
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dword %0, off"
-      :
-      : "v"(addr), "s"(lds)
-      : "m0");
+      "global_load_lds_dword %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(keep)
+      : "v"(addr), "s"(lds));
 }
 template <int N>
 __device__ __forceinline__ void wait_vm() {
@@ -345,12 +349,19 @@ struct Wide {
   static constexpr int kRowBytes = kD * kEB;        // 1152 | 576 per cached token
   static constexpr int kABytes = kDC * kEB;         // 1024 | 512: latent part of a row
   static constexpr int kRows = 32;                  // tokens per chunk
-  static constexpr int kRegB = kRows * kABytes;     // region B (RoPE part) offset
-  static constexpr int kScaleOff = kRegB + kRows * kDR * kEB;
-  static constexpr int kSlotBytes = kScaleOff + (FP8 ? 128 : 0);
+  // Multi-wave workgroups pipeline each chunk's P.V into the next chunk's
+  // step, where it overlaps the softmax (one barrier per chunk).
+  static constexpr bool kPipe = R == 4 && !FP8;
+  // A chunk occupies one block of the region-A ring (latent part, also the
+  // P.V operand) and one block of the region-B ring (RoPE part, fp8 scales),
+  // which is free as soon as the scores are done.
+  static constexpr int kABlk = kRows * kABytes;
+  static constexpr int kScaleOffB = kRows * kDR * kEB;  // fp8 scales in a region-B block
+  static constexpr int kBBlk = kScaleOffB + (FP8 ? 128 : 0);
   // One-wave workgroups (units of <= 32 rows) run four to a compute unit
   // (fp8; bf16 slots fit two) and keep two chunks in LDS.
   static constexpr int kSlots = (R == 1) ? 2 : 4;
+  static constexpr int kSlotsB = kPipe ? kSlots - 1 : kSlots;
   static constexpr int kNA = FP8 ? 16 : 32;         // 1 KB copies of region A
   static constexpr int kNB = FP8 ? 2 : 4;           // 1 KB copies of region B
   static constexpr int kNCopy = kNA + kNB + (FP8 ? 1 : 0);  // (+ the 32 scales)
@@ -359,21 +370,29 @@ struct Wide {
   static constexpr int kPerWave = (kNCopy + R - 1) / R;
   static_assert(kNA % R == 0, "region-A copies must split evenly over the waves");
   static constexpr int kLook = SPARSE ? 2 : 0;      // lookup copies per step (wave 0)
-  static constexpr int kLeadDma = kSlots - 1;
+  // Copies of item z are issued while item z - kLeadDma is computed: the
+  // pipelined step also still reads item z - kLeadDma - 1 (its P.V).
+  static constexpr int kLeadDma = kPipe ? kSlots - 2 : kSlots - 1;
   static constexpr int kLeadPage = 2 * kLeadDma;
   static constexpr int kLeadCur = SPARSE ? 3 * kLeadDma : kLeadPage;
-  static constexpr int kRing = SPARSE ? 16 : 8;
+  static constexpr int kRing = kLeadCur < 8 ? 8 : 16;
   static_assert(kRing > kLeadCur, "descriptor ring too short");
-  static constexpr int kDescOff = kSlots * kSlotBytes;
-  static constexpr int kIdxOff = kDescOff + kRing * 32;
+  static constexpr int kBOff = kSlots * kABlk;
+  static constexpr int kDescOff = kBOff + kSlotsB * kBBlk;
+  static constexpr int kIdxOff = kDescOff + (SPARSE ? kRing * 32 : 0);
   static constexpr int kPgOff = kIdxOff + (SPARSE ? kRing * 128 : 0);
   static constexpr int kPOff = kPgOff + (SPARSE ? kRing * 128 : 0);
-  static constexpr int kAlphaOff = kPOff + 32 * R * 64;
-  static constexpr int kMrgOff = kAlphaOff + 32 * R * 4;
+  // P and the rescale factors are double-buffered when pipelined (chunk s
+  // writes them while chunk s-1's are read); the end-of-segment merge
+  // buffers then reuse the rescale buffers.
+  static constexpr int kNPBuf = kPipe ? 2 : 1;
+  static constexpr int kPBytes = 32 * R * 64;
+  static constexpr int kAlphaOff = kPOff + kNPBuf * kPBytes;
+  static constexpr int kMrgOff = kPipe ? kAlphaOff : kAlphaOff + 32 * R * 4;
   static constexpr int kDummyOff = kMrgOff + 2 * 32 * R * 4;
   static constexpr int kLdsBytes = kDummyOff + 64;
   static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
-  static_assert(kSlotBytes % 16 == 0, "slot alignment");
+  static_assert(kABlk % 1024 == 0 && kBBlk % 16 == 0 && kBOff % 16 == 0, "block alignment");
   // vector-memory operations wave w issues per step: its copies, plus the
   // lookups of wave 0
   static constexpr int per_step(int w) { return kPerWave + (w == 0 ? kLook : 0); }
@@ -389,12 +408,16 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
   const int g = lane >> 5, l32 = lane & 31;
   const int wg = xcd_logical(blockIdx.x, gridDim.x);
 
-  uint8_t* const slots = lds;
+  // Item z's blocks in the two rings, its P buffer and rescale factors.
+  auto blk_a = [&](int z) -> uint8_t* { return lds + (z % W::kSlots) * W::kABlk; };
+  auto blk_b = [&](int z) -> uint8_t* { return lds + W::kBOff + (z % W::kSlotsB) * W::kBBlk; };
+  auto pbuf_of = [&](int z) -> uint8_t* { return lds + W::kPOff + (W::kPipe ? (z & 1) * W::kPBytes : 0); };
+  auto alpha_of = [&](int z) -> float* {
+    return reinterpret_cast<float*>(lds + W::kAlphaOff + (W::kPipe ? (z & 1) * 32 * R * 4 : 0));
+  };
   int* const desc_ring = reinterpret_cast<int*>(lds + W::kDescOff);
   int* const idx_ring = reinterpret_cast<int*>(lds + W::kIdxOff);
   int* const pg_ring = reinterpret_cast<int*>(lds + W::kPgOff);
-  uint8_t* const pbuf = lds + W::kPOff;
-  float* const alpha_buf = reinterpret_cast<float*>(lds + W::kAlphaOff);
   float* const mrg = reinterpret_cast<float*>(lds + W::kMrgOff);
   int* const dummy = reinterpret_cast<int*>(lds + W::kDummyOff);
   auto desc = [&](int x) -> int* { return desc_ring + (x & (W::kRing - 1)) * 8; };
@@ -545,10 +568,10 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
     }
     return r;
   };
-  // This wave's j-th copy of an item into the slot at LDS address `slot`.
-  // Copy i = j*R + rg of an item: region-A copies first, then region B, the
-  // fp8 scales, and padding.
-  auto copy = [&](int j, uint32_t slot, const Src& sr) {
+  // This wave's j-th copy of an item into its blocks at LDS addresses
+  // slot (region A) and slotb (region B).  Copy i = j*R + rg of an item:
+  // region-A copies first, then region B, the fp8 scales, and padding.
+  auto copy = [&](int j, uint32_t slot, uint32_t slotb, const Src& sr) {
     int ln = lane;
     asm volatile("" : "+v"(ln));  // keeps per-lane offsets from being hoisted out of the loop
     const uint8_t* zero = a.ws_zero;
@@ -580,7 +603,7 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
       const int jb = i - W::kNA;
       const int row = FP8 ? 16 * jb + (ln >> 2) : 8 * jb + (ln >> 3);
       const int c = FP8 ? ((ln & 3) ^ (row & 3)) : ((ln & 7) ^ ((row >> 1) & 7));
-      copy16_v(rowsrc(row, (uint32_t)(W::kABytes + (c << 4))), slot + W::kRegB + jb * 1024);
+      copy16_v(rowsrc(row, (uint32_t)(W::kABytes + (c << 4))), slotb + jb * 1024);
     };
     if constexpr (!FP8 && W::kNCopy % R == 0) {
       region_b();
@@ -592,7 +615,7 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
           const float* src;
           if constexpr (!SPARSE) src = ln < sr.nvalid ? sr.scales + ln : reinterpret_cast<const float*>(zero);
           else src = sr.tok >= 0 ? a.kv_scales + sr.tok : reinterpret_cast<const float*>(zero);
-          copy4_v(src, slot + W::kScaleOff);
+          copy4_v(src, slotb + W::kScaleOffB);
         }
       } else if (ln == 0) {
         copy4_v(zero, lds_addr(dummy));
@@ -600,9 +623,9 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
     }
   };
   auto copy_all = [&](int z, const Src& sr) {
-    const uint32_t slot = lds_addr(slots + (z % W::kSlots) * W::kSlotBytes);
+    const uint32_t slot = lds_addr(blk_a(z)), slotb = lds_addr(blk_b(z));
 #pragma unroll
-    for (int j = 0; j < W::kPerWave; j++) copy(j, slot, sr);
+    for (int j = 0; j < W::kPerWave; j++) copy(j, slot, slotb, sr);
   };
   // Wait until this wave's copies of the item about to be computed (and
   // everything it issued before them) have landed: exactly
@@ -662,33 +685,20 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
   // Per-lane pieces of the swizzled LDS addresses.
   const int ya = g ^ (FP8 ? 0 : sw16(l32));  // bf16 region A (score operand)
   const int yb = g ^ ((l32 >> 1) & 7);       // bf16 region B
-  // ------------------------------------------------------------ one step
-  // Computes item s (in `cur`) and issues this wave's copies of item z into
-  // `nxt` between the score MFMAs.
-  auto step = [&](const uint8_t* __restrict__ cur, uint32_t nxt, const Src& sr, int s, int nv,
-                  int rem, const UnitInfo& ui) {
-    // dense: nv visible rows at the chunk's start, rem = length - first token
-    int lim = 0;
-    unsigned vm = 0;
-    if constexpr (!SPARSE) {
-      lim = nv;
-      if (a.causal) {
-        const int srow = (ui.rin_b0 + rg * kRowsPerWave + l32) / a.H;
-        lim = min(lim, rem - a.Sq + srow + 1);
-      }
-    } else {
-      vm = (unsigned)__builtin_amdgcn_readfirstlane(desc(s)[4]) >> (4 * g);
-    }
-    // A chunk with nothing visible is computed like any other: its rows
-    // are zero in LDS and every weight comes out 0.
-    constexpr int kEvery = 36 / W::kPerWave;  // MFMAs between two copies
+  // ------------------------------------------------------------ step pieces
+  // Item s lives in region-A block curA and region-B block curB; a step is
+  // qk (scores, with this wave's copies of item s + kLeadDma issued between
+  // the MFMAs), softmax (P and rescale factors to LDS), and after a barrier
+  // rescale + pv (O += P.V).  Pipelined, the P.V of item s-1 runs beside the
+  // softmax of item s instead.
 
-    // ---- S^T[token][row] = K . Q^T over 576 dims, tokens l32 of the chunk.
-    // K operands stream through a ring of kRing registers with kLead reads
-    // in flight; a register is refilled two MFMAs after its last use.
+  // ---- S^T[token][row] = K . Q^T over 576 dims, tokens l32 of the chunk.
+  // K operands stream through a ring of kRingK registers with kLead reads
+  // in flight; a register is refilled two MFMAs after its last use.
+  auto qk = [&](uint32_t curA, uint32_t curB, uint32_t nxtA, uint32_t nxtB, const Src& sr) -> f32x16 {
+    constexpr int kEvery = 36 / W::kPerWave;  // MFMAs between two copies
     f32x16 sacc = {};
     constexpr int kLead = 6, kRingK = 8;
-    const uint32_t cur_a = lds_addr(cur);
     // Dense: no wait here.  A scalar load still in flight (the block table)
     // only makes the counted waits below stricter, never looser, since LDS
     // operations complete in order.
@@ -696,9 +706,9 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
     if constexpr (!FP8) {
       uint32_t adA[8], adB[4];
 #pragma unroll
-      for (int k = 0; k < 8; k++) adA[k] = cur_a + l32 * 1024 + (((2 * k) ^ ya) << 4);
+      for (int k = 0; k < 8; k++) adA[k] = curA + l32 * 1024 + (((2 * k) ^ ya) << 4);
 #pragma unroll
-      for (int k = 0; k < 4; k++) adB[k] = cur_a + W::kRegB + l32 * 128 + (((2 * k) ^ yb) << 4);
+      for (int k = 0; k < 4; k++) adB[k] = curB + l32 * 128 + (((2 * k) ^ yb) << 4);
       bf16x8 ring[kRingK];
       auto rd = [&](auto KS) {
         constexpr int ks = decltype(KS)::value;
@@ -709,16 +719,16 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
       unroll<36>([&](auto KS) {
         constexpr int ks = decltype(KS)::value;
         lds_ready<(kLead - 1 < 35 - ks ? kLead - 1 : 35 - ks)>(ring[ks % kRingK]);
-        if constexpr (ks % kEvery == 0 && ks / kEvery < W::kPerWave) copy(ks / kEvery, nxt, sr);
+        if constexpr (ks % kEvery == 0 && ks / kEvery < W::kPerWave) copy(ks / kEvery, nxtA, nxtB, sr);
         sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[ks % kRingK], qf[ks], sacc, 0, 0, 0);
         if constexpr (ks + kLead < 36) rd(std::integral_constant<int, ks + kLead>{});
       });
     } else {
       uint32_t adA[8], adB[4];
 #pragma unroll
-      for (int k = 0; k < 8; k++) adA[k] = cur_a + l32 * 512 + 8 * g + ((k ^ (l32 & 7)) << 4);
+      for (int k = 0; k < 8; k++) adA[k] = curA + l32 * 512 + 8 * g + ((k ^ (l32 & 7)) << 4);
 #pragma unroll
-      for (int k = 0; k < 4; k++) adB[k] = cur_a + W::kRegB + l32 * 64 + 8 * g + ((k ^ (l32 & 3)) << 4);
+      for (int k = 0; k < 4; k++) adB[k] = curB + l32 * 64 + 8 * g + ((k ^ (l32 & 3)) << 4);
       u32x2 ring[kRingK];
       auto rd = [&](auto KS) {
         constexpr int ks = decltype(KS)::value;
@@ -729,18 +739,45 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
       unroll<36>([&](auto KS) {
         constexpr int ks = decltype(KS)::value;
         lds_ready<(kLead - 1 < 35 - ks ? kLead - 1 : 35 - ks)>(ring[ks % kRingK]);
-        if constexpr (ks % kEvery == 0 && ks / kEvery < W::kPerWave) copy(ks / kEvery, nxt, sr);
+        if constexpr (ks % kEvery == 0 && ks / kEvery < W::kPerWave) copy(ks / kEvery, nxtA, nxtB, sr);
         const bf16x8 kf = cvt8_fp8(ring[ks % kRingK]);
         sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc, 0, 0, 0);
         if constexpr (ks + kLead < 36) rd(std::integral_constant<int, ks + kLead>{});
       });
     }
+    return sacc;
+  };
 
-    // ---- online softmax: lane holds row l32, tokens 8*(i/4) + 4g + i%4.
-    // fp8: token scales multiply the scores and, before P.V, the weights.
-    // The row maximum is taken over the unscaled scores (the softmax scale
-    // is positive) and the scale enters each weight's exponent in one FMA.
-    const float* scl = reinterpret_cast<const float*>(cur + W::kScaleOff) + 4 * g;
+  // Causal masking: row r of a unit sees cached tokens below
+  // rem + coff(r) of a chunk (coff = 1 + its query position - Sq);
+  // without masking coff is large enough never to bind.
+  int coff = 1 << 30;
+  auto set_coff = [&](const UnitInfo& u) {
+    if (a.causal) {
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      coff = 1 + (u.rin_b0 + rg * kRowsPerWave + (ln & 31)) / a.H - a.Sq;
+    }
+  };
+
+  // ---- online softmax of item s: lane holds row l32, tokens
+  // 8*(i/4) + 4g + i%4.  Writes P (bf16) to `pb` and the rows' rescale
+  // factors to `ab`.  Dense: nv visible rows at the chunk's start, rem =
+  // length - first token.  A chunk with nothing visible is computed like any
+  // other: its rows are zero in LDS and every weight comes out 0.
+  // fp8: token scales multiply the scores and, before P.V, the weights.
+  // The row maximum is taken over the unscaled scores (the softmax scale
+  // is positive) and the scale enters each weight's exponent in one FMA.
+  auto softmax = [&](f32x16 sacc, const uint8_t* curB, int s, int nv, int rem, uint8_t* pb,
+                     float* ab) {
+    int lim = 0;
+    unsigned vm = 0;
+    if constexpr (!SPARSE) {
+      lim = min(nv, rem + coff);
+    } else {
+      vm = (unsigned)__builtin_amdgcn_readfirstlane(desc(s)[4]) >> (4 * g);
+    }
+    const float* scl = reinterpret_cast<const float*>(curB + W::kScaleOffB) + 4 * g;
     const float c2 = a.scale_log2;
     float mloc = kNegInf;
 #pragma unroll
@@ -764,13 +801,13 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
     const float mnew = fmaxf(m_run, mt);
     const bool need = mnew > m_run + kRescaleSlack;  // -inf + slack = -inf
     const bool moved = __builtin_amdgcn_ballot_w64(need) != 0;
-    float alpha = 1.f;  // exactly 1 unless this row's maximum moved
-    if (moved) {
-      // A row with no finite score yet has O = 0 and l = 0: nothing to scale.
-      alpha = (m_run == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run - mnew);
-      l_run *= alpha;
-      m_run = mnew;
-    }
+    // alpha is exactly 1 unless this row's maximum moved; a row with no
+    // finite score yet has O = 0 and l = 0: nothing to scale.  Selects, not
+    // branches, so that this code can interleave with other work.
+    const float ex = __builtin_amdgcn_exp2f(m_run - mnew);
+    const float alpha = (moved && m_run != kNegInf) ? ex : 1.f;
+    l_run *= alpha;
+    m_run = moved ? mnew : m_run;
     const float muse = (m_run == kNegInf) ? 0.f : m_run;
     float psum = 0.f;
     bf16x8 pf[2];
@@ -789,23 +826,23 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
     }
     l_run += psum;
 
-    // ---- P (bf16) and the rescale factors of this wave's rows go through
-    // LDS: row r, 16-byte chunk (g, kk) at position (2g + kk) ^ ((r >> 2) & 3).
+    // P row r, 16-byte chunk (g, kk) at position (2g + kk) ^ ((r >> 2) & 3).
     const int pc = (l32 >> 2) & 3;
-    uint8_t* prow = pbuf + (32 * rg + l32) * 64;
+    uint8_t* prow = pb + (32 * rg + l32) * 64;
     *reinterpret_cast<bf16x8*>(prow + (((2 * g) ^ pc) << 4)) = pf[0];
     *reinterpret_cast<bf16x8*>(prow + (((2 * g + 1) ^ pc) << 4)) = pf[1];
-    if (g == 0) alpha_buf[32 * rg + l32] = alpha;
-    wait_lds();
-    barrier();
+    ab[32 * rg + l32] = alpha;  // both halves of a row hold the same value
+  };
+
+  // ---- O *= alpha for every row whose maximum moved (rare).
+  auto rescale = [&](const float* ab) {
     float al[R];
     bool scale_any = false;
 #pragma unroll
     for (int rb = 0; rb < R; rb++) {
-      al[rb] = alpha_buf[32 * rb + l32];
+      al[rb] = ab[32 * rb + l32];
       scale_any |= al[rb] != 1.f;
     }
-    // Rare: some row's maximum moved after it had seen a finite score.
     if (__builtin_amdgcn_ballot_w64(scale_any) != 0) {
 #pragma unroll
       for (int rb = 0; rb < R; rb++) {
@@ -813,13 +850,20 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
         for (int dbl = 0; dbl < DB; dbl++) acc_scale(o[dbl * R + rb], al[rb]);
       }
     }
+  };
 
+  // ---- O^T[dim][row] += V^T[dim][token] . P^T[token][row] for the item
+  // whose region-A block is `cur` and whose P is in `pb`; k-step kk covers
+  // tokens 16kk..16kk+15 in the accumulator order of S^T.
+  auto pv = [&](const uint8_t* __restrict__ cur, const uint8_t* pb) {
     // Lane offsets of the transposed V reads, recomputed here from a
     // laundered lane index so that they are not held (beside Q) through the
     // score loop, where registers are scarcest.
     int lnv = lane;
     asm volatile("" : "+v"(lnv));
     const int G16v = lnv >> 4, i16v = lnv & 15;
+    const int l32v = lnv & 31, gv = lnv >> 5;
+    const int pc = (l32v >> 2) & 3;
     int vbase = 0, vy0 = 0, vy1 = 0;
     int voff8[4] = {0, 0, 0, 0};
     if constexpr (!FP8) {
@@ -836,9 +880,6 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
 #pragma unroll
       for (int p4 = 0; p4 < 4; p4++) voff8[p4] = trow * 512 + (((2 * p4 + (G16v & 1)) ^ z8) << 4) + 8 * (i16v & 1);
     }
-
-    // ---- O^T[dim][row] += V^T[dim][token] . P^T[token][row]; k-step kk
-    // covers tokens 16kk..16kk+15 in the accumulator order of S^T.
     auto vload = [&](int kk, int db) -> bf16x8 {
       if constexpr (!FP8) {
         const uint8_t* p0 = cur + vbase + (16 * kk) * 1024 + 256 * (db >> 2) + (((4 * (db & 3)) ^ vy0) << 4);
@@ -853,17 +894,17 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
     };
 #pragma unroll
     for (int kk = 0; kk < 2; kk++) {
-      bf16x8 pb[R], vv[DB];
+      bf16x8 pbv[R], vv[DB];
 #pragma unroll
       for (int rb = 0; rb < R; rb++)
-        pb[rb] = *reinterpret_cast<const bf16x8*>(pbuf + (32 * rb + l32) * 64 + (((2 * g + kk) ^ pc) << 4));
+        pbv[rb] = *reinterpret_cast<const bf16x8*>(pb + (32 * rb + l32v) * 64 + (((2 * gv + kk) ^ pc) << 4));
 #pragma unroll
       for (int dbl = 0; dbl < DB; dbl++) vv[dbl] = vload(kk, DB * rg + dbl);
 #pragma unroll
       for (int dbl = 0; dbl < DB; dbl++)
 #pragma unroll
         for (int rb = 0; rb < R; rb++)
-          o[dbl * R + rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv[dbl], pb[rb], o[dbl * R + rb], 0, 0, 0);
+          o[dbl * R + rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv[dbl], pbv[rb], o[dbl * R + rb], 0, 0, 0);
     }
   };
 
@@ -880,6 +921,10 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
     const float lt = pair_sum(l_run);
     float* mm = mrg;
     float* ll = mrg + 32 * R;
+    if constexpr (W::kPipe) {  // the merge buffers are the rescale buffers
+      wait_lds();
+      barrier();
+    }
     if (g == 0) {
       mm[32 * rg + l32] = m_run;
       ll[32 * rg + l32] = lt;
@@ -988,46 +1033,85 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
     load_q(ui);
     take_q();
   }
+  // Set-up of item s at the top of its step: where the copies of item
+  // s + kLeadDma come from, and (dense) the rows item s shows.
+  Src sr;
+  int nv = 0, rem = 0;
+  DD nd{};
+  auto begin_item = [&]() {
+    const int z = s + W::kLeadDma;
+    if constexpr (SPARSE) {
+      lookup(s + W::kLeadCur);
+      next();
+      page_lookup(s + W::kLeadPage);
+      sr = source(z, dz);
+    } else {
+      // Item s + kQ enters the queue at the end of this step.  Its block
+      // table entry is requested here, a whole step before the queue
+      // shift copies it (the copy waits for the scalar load to land).
+      nd = cursor_desc();
+      next();
+      sr = source_dense(fq[W::kLeadDma]);
+      nv = dd_nvalid(fq[0]);
+      rem = fq[0].remh >> 1;
+    }
+  };
+  auto scores = [&]() -> f32x16 {
+    const int z = s + W::kLeadDma;
+    f32x16 r = qk(lds_addr(blk_a(s)), lds_addr(blk_b(s)), lds_addr(blk_a(z)), lds_addr(blk_b(z)), sr);
+    // In ordinary registers, so that O keeps the accumulation registers
+    // while the scores wait for their softmax.
+    if constexpr (W::kPipe) asm volatile("" : "+v"(r));
+    return r;
+  };
+  auto end_item = [&]() {
+    s++;
+    wait_item();
+    wait_lds();
+    barrier();  // item s is in LDS for every wave; step s-1 is done everywhere
+    if constexpr (SPARSE) {
+      dc = read_desc(s);
+      dz = read_desc(s + W::kLeadDma);
+    } else {
+#pragma unroll
+      for (int i = 0; i + 1 < kQ; i++) fq[i] = fq[i + 1];
+      fq[kQ - 1] = nd;
+      dc.u = fq[0].u;
+    }
+  };
 #pragma unroll 1
   while (uu >= 0) {
     reset();
+    set_coff(ui);
+    if constexpr (W::kPipe) {
+      // The unit's first item: nothing to multiply into O yet.
+      begin_item();
+      softmax(scores(), blk_b(s), s, nv, rem, pbuf_of(s), alpha_of(s));
+      end_item();
 #pragma unroll 1
-    do {
-      const int z = s + W::kLeadDma;
-      Src sr;
-      int nv = 0, rem = 0;
-      DD nd{};
-      if constexpr (SPARSE) {
-        lookup(s + W::kLeadCur);
-        next();
-        page_lookup(s + W::kLeadPage);
-        sr = source(z, dz);
-      } else {
-        // Item s + kQ enters the queue at the end of this step.  Its block
-        // table entry is requested here, a whole step before the queue
-        // shift copies it (the copy waits for the scalar load to land).
-        nd = cursor_desc();
-        next();
-        sr = source_dense(fq[W::kLeadDma]);
-        nv = dd_nvalid(fq[0]);
-        rem = fq[0].remh >> 1;
+      while (dc.u == uu) {
+        begin_item();
+        const f32x16 sacc = scores();
+        rescale(alpha_of(s - 1));
+        pv(blk_a(s - 1), pbuf_of(s - 1));
+        softmax(sacc, blk_b(s), s, nv, rem, pbuf_of(s), alpha_of(s));
+        end_item();
       }
-      step(slots + (s % W::kSlots) * W::kSlotBytes, lds_addr(slots + (z % W::kSlots) * W::kSlotBytes),
-           sr, s, nv, rem, ui);
-      s++;
-      wait_item();
-      wait_lds();
-      barrier();  // item s is in LDS for every wave; step s-1 is done everywhere
-      if constexpr (SPARSE) {
-        dc = read_desc(s);
-        dz = read_desc(s + W::kLeadDma);
-      } else {
-#pragma unroll
-        for (int i = 0; i + 1 < kQ; i++) fq[i] = fq[i + 1];
-        fq[kQ - 1] = nd;
-        dc.u = fq[0].u;
-      }
-    } while (dc.u == uu);
+      // The unit's last item.
+      rescale(alpha_of(s - 1));
+      pv(blk_a(s - 1), pbuf_of(s - 1));
+    } else {
+#pragma unroll 1
+      do {
+        begin_item();
+        softmax(scores(), blk_b(s), s, nv, rem, pbuf_of(s), alpha_of(s));
+        wait_lds();
+        barrier();
+        rescale(alpha_of(s));
+        pv(blk_a(s), pbuf_of(s));
+        end_item();
+      } while (dc.u == uu);
+    }
     const UnitInfo done = ui;
     if (dc.u >= 0) {
       ui = unit_info(a, SPARSE, dc.u);

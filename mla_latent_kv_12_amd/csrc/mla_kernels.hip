@@ -236,47 +236,57 @@ __device__ __forceinline__ int xcd_logical(int i, int G) {
 // Direct HBM -> LDS copies, written as inline assembly: the kernel counts
 // them itself (s_waitcnt vmcnt with the exact number of younger copies), so
 // the compiler must neither wait for them on its own nor move them across
-// the explicit waits.  Each copy points M0 at the LDS destination (every
-// active lane writes M0 + 4*lane words of its size) and restores M0.
+// the explicit waits.  M0 holds the LDS destination (every active lane
+// writes M0 + size*lane); it is an input operand, so the compiler sets it
+// and knows the assembly leaves it unchanged.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)reinterpret_cast<uintptr_t>(p);
 }
 // 16 bytes per lane from a wave-uniform base plus a per-lane byte offset.
 __device__ __forceinline__ void copy16_s(const void* base, uint32_t voff, uint32_t lds) {
-  uint32_t keep;
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %2\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(keep)
-      : "v"(voff), "s"(base), "s"(lds));
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(voff), "s"(base), "{m0}"(lds));
+}
+// 16 bytes per lane through a raw buffer resource (stride 0): a lane whose
+// offset is at or past the resource's size reads zeros (the hardware range
+// check), so rows past a sequence's end need no address of their own.
+__device__ __forceinline__ void copy16_b(i32x4 rsrc, uint32_t voff, uint32_t lds) {
+  asm volatile(
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %0, %1, 0 offen lds"
+      :
+      : "v"(voff), "s"(rsrc), "{m0}"(lds));
+}
+// Raw buffer resource over `bytes` bytes from `base` (gfx9 word 3: untyped
+// 32-bit data, no swizzle); every word is wave-uniform.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(b >> 32) & 0xffffu));
+  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+  r[3] = 0x00020000;
+  return r;
 }
 // 16 bytes per lane from a per-lane address.
 __device__ __forceinline__ void copy16_v(const void* addr, uint32_t lds) {
-  uint32_t keep;
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(keep)
-      : "v"(addr), "s"(lds));
+      "global_load_lds_dwordx4 %0, off"
+      :
+      : "v"(addr), "{m0}"(lds));
 }
 // 4 bytes per lane from a per-lane address.
 __device__ __forceinline__ void copy4_v(const void* addr, uint32_t lds) {
-  uint32_t keep;
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dword %1, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(keep)
-      : "v"(addr), "s"(lds));
+      "global_load_lds_dword %0, off"
+      :
+      : "v"(addr), "{m0}"(lds));
 }
 template <int N>
 __device__ __forceinline__ void wait_vm() {
@@ -409,8 +419,9 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
   const int wg = xcd_logical(blockIdx.x, gridDim.x);
 
   // Item z's blocks in the two rings, its P buffer and rescale factors.
-  auto blk_a = [&](int z) -> uint8_t* { return lds + (z % W::kSlots) * W::kABlk; };
-  auto blk_b = [&](int z) -> uint8_t* { return lds + W::kBOff + (z % W::kSlotsB) * W::kBBlk; };
+  // (item numbers are never negative: unsigned remainders are cheaper)
+  auto blk_a = [&](int z) -> uint8_t* { return lds + ((unsigned)z % W::kSlots) * W::kABlk; };
+  auto blk_b = [&](int z) -> uint8_t* { return lds + W::kBOff + ((unsigned)z % W::kSlotsB) * W::kBBlk; };
   auto pbuf_of = [&](int z) -> uint8_t* { return lds + W::kPOff + (W::kPipe ? (z & 1) * W::kPBytes : 0); };
   auto alpha_of = [&](int z) -> float* {
     return reinterpret_cast<float*>(lds + W::kAlphaOff + (W::kPipe ? (z & 1) * 32 * R * 4 : 0));
@@ -539,20 +550,22 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
     const float* scales;  // dense fp8: first scale of the chunk
     int nvalid;           // dense: visible rows at the start of the chunk
     int tok;              // sparse: token (page*64 + row) of row `lane` (< 32), or -1
+    i32x4 rsrc;           // dense bf16: the chunk's visible rows as a buffer resource
   };
   // Where item z's rows come from (read from its descriptor and rings).
   auto source_dense = [&](const DD& d) -> Src {
-    Src r{a.ws_zero, reinterpret_cast<const float*>(a.ws_zero), 0, -1};
+    Src r{a.ws_zero, reinterpret_cast<const float*>(a.ws_zero), 0, -1, {}};
     r.nvalid = dd_nvalid(d);
     if (r.nvalid > 0) {
       const int half = d.remh & 1;
       r.base = a.kv + (size_t)d.pg * (kPage * W::kRowBytes) + half * 32 * W::kRowBytes;
       r.scales = a.kv_scales + (size_t)d.pg * kPage + half * 32;
     }
+    if constexpr (!FP8) r.rsrc = make_rsrc(r.base, (uint32_t)r.nvalid * W::kRowBytes);
     return r;
   };
   auto source = [&](int z, const Desc& dz) -> Src {
-    Src r{a.ws_zero, reinterpret_cast<const float*>(a.ws_zero), 0, -1};
+    Src r{a.ws_zero, reinterpret_cast<const float*>(a.ws_zero), 0, -1, {}};
     const int uu = dz.u, th = dz.th, LL = dz.L;
     {
       int ln = lane;
@@ -585,14 +598,14 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
     const int i = j * R + rg;
     if (j < W::kNA / R) {
       if constexpr (!FP8) {  // row i, lane = 16-byte chunk position
-        const uint8_t* src;
         if constexpr (!SPARSE) {
-          src = i < sr.nvalid ? sr.base + i * W::kRowBytes : zero;
+          // rows at or past nvalid fall outside the resource and read zeros
+          copy16_b(sr.rsrc, (uint32_t)(((ln ^ sw16(i)) << 4) + i * W::kRowBytes), slot + i * 1024);
         } else {
           const int t = __builtin_amdgcn_readlane(sr.tok, i);
-          src = t >= 0 ? a.kv + (size_t)t * W::kRowBytes : zero;
+          const uint8_t* src = t >= 0 ? a.kv + (size_t)t * W::kRowBytes : zero;
+          copy16_s(src, (uint32_t)((ln ^ sw16(i)) << 4), slot + i * 1024);
         }
-        copy16_s(src, (uint32_t)((ln ^ sw16(i)) << 4), slot + i * 1024);
       } else {  // rows 2i and 2i+1, 32 lanes each
         const int row = 2 * i + (ln >> 5);
         copy16_v(rowsrc(row, (uint32_t)(((ln & 31) ^ (row & 7)) << 4)), slot + i * 1024);
@@ -603,7 +616,10 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
       const int jb = i - W::kNA;
       const int row = FP8 ? 16 * jb + (ln >> 2) : 8 * jb + (ln >> 3);
       const int c = FP8 ? ((ln & 3) ^ (row & 3)) : ((ln & 7) ^ ((row >> 1) & 7));
-      copy16_v(rowsrc(row, (uint32_t)(W::kABytes + (c << 4))), slotb + jb * 1024);
+      if constexpr (!FP8 && !SPARSE)
+        copy16_b(sr.rsrc, (uint32_t)(row * W::kRowBytes + W::kABytes + (c << 4)), slotb + jb * 1024);
+      else
+        copy16_v(rowsrc(row, (uint32_t)(W::kABytes + (c << 4))), slotb + jb * 1024);
     };
     if constexpr (!FP8 && W::kNCopy % R == 0) {
       region_b();

@@ -313,6 +313,25 @@ template <int N, typename V>
 __device__ __forceinline__ void lds_ready(V& v) {
   asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(v) : "n"(N));
 }
+// Score MFMAs with the accumulator in ordinary registers (the accumulation
+// registers all hold O).  Back-to-back MFMAs accumulating into exactly the
+// same registers need no wait states; the first of a chain starts from 0;
+// mfma_settle() supplies the wait states a VALU read of the result needs
+// after the last one (more than the 8-pass 32x32x16 MFMA requires).
+__device__ __forceinline__ void mfma_first(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_acc(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_settle(f32x16& acc) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(acc));
+}
+// The same for two registers about to be used.
+template <int N, typename V>
+__device__ __forceinline__ void lds_ready2(V& v, V& w) {
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(v), "+v"(w) : "n"(N));
+}
 template <typename F, int... I>
 __device__ __forceinline__ void unroll_impl(F&& f, std::integer_sequence<int, I...>) {
   (f(std::integral_constant<int, I>{}), ...);
@@ -734,11 +753,15 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
       unroll<kLead>(rd);
       unroll<36>([&](auto KS) {
         constexpr int ks = decltype(KS)::value;
-        lds_ready<(kLead - 1 < 35 - ks ? kLead - 1 : 35 - ks)>(ring[ks % kRingK]);
+        // one wait per pair of MFMAs: operands ks and ks+1 have landed
+        if constexpr (ks % 2 == 0)
+          lds_ready2<(kLead - 2 < 34 - ks ? kLead - 2 : 34 - ks)>(ring[ks % kRingK], ring[(ks + 1) % kRingK]);
         if constexpr (ks % kEvery == 0 && ks / kEvery < W::kPerWave) copy(ks / kEvery, nxtA, nxtB, sr);
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[ks % kRingK], qf[ks], sacc, 0, 0, 0);
+        if constexpr (ks == 0) mfma_first(sacc, ring[0], qf[0]);
+        else mfma_acc(sacc, ring[ks % kRingK], qf[ks]);
         if constexpr (ks + kLead < 36) rd(std::integral_constant<int, ks + kLead>{});
       });
+      mfma_settle(sacc);
     } else {
       uint32_t adA[8], adB[4];
 #pragma unroll
@@ -796,6 +819,25 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
     const float* scl = reinterpret_cast<const float*>(curB + W::kScaleOffB) + 4 * g;
     const float c2 = a.scale_log2;
     float mloc = kNegInf;
+    // Dense chunks whose 32 tokens are all visible to every row of the wave
+    // (the common case) skip the masks.  Not in the pipelined kernel: there
+    // the branch would split the block in which this softmax interleaves
+    // with the previous chunk's P.V MFMAs (measured slower).
+    bool full = false;
+    if constexpr (!SPARSE && !W::kPipe) full = __builtin_amdgcn_ballot_w64(lim < 32) == 0;
+    if (full) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; q4++) {
+        f32x4 sv = {1.f, 1.f, 1.f, 1.f};
+        if constexpr (FP8) sv = *reinterpret_cast<const f32x4*>(scl + 8 * q4);
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          const int i = 4 * q4 + e;
+          if constexpr (FP8) sacc[i] *= sv[e];
+          mloc = fmaxf(mloc, sacc[i]);
+        }
+      }
+    } else {
 #pragma unroll
     for (int q4 = 0; q4 < 4; q4++) {
       f32x4 sv = {1.f, 1.f, 1.f, 1.f};
@@ -812,6 +854,7 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
         sacc[i] = ok ? v : kNegInf;
         mloc = fmaxf(mloc, sacc[i]);
       }
+    }
     }
     const float mt = pair_max(mloc) * c2;  // -inf stays -inf
     const float mnew = fmaxf(m_run, mt);

@@ -111,6 +111,50 @@ def cpu_baseline(inp, target_s: float):
             "sample": f"first {n} of {per_row_flop.size} query rows (all their visible tokens), fp64"}
 
 
+def bench_append(args):
+    """Times mla_kv_append of the workload's B*Sq new rows into its cache.
+
+    Algorithmic bytes per row: the new bf16 row read (1152 B), the block-table
+    entry and length read (8 B), the row written (1152 B bf16, or 576 B codes
+    + 4 B scale fp8)."""
+    import mla_latent_kv_12_amd as mla
+    dev = torch.device("cuda:0")
+    inp = S.make_inputs(S.config(args.workload), poison=False)
+    B, Sq = inp["B"], inp["Sq"]
+    fp8 = inp["kv_dtype"] == "fp8"
+    kv = inp["kv_pages"].to(dev)
+    sc = inp["kv_scales"].to(dev) if fp8 else None
+    bt, L = inp["block_table"].to(dev), inp["cache_seqlens"].to(dev)
+    new = S._randn_bf16((B, Sq, 576), torch.Generator().manual_seed(99)).to(dev)
+    for _ in range(args.warmup):
+        mla.kv_append(new, kv, bt, L, kv_scales=sc)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for a, b in evs:
+        a.record()
+        mla.kv_append(new, kv, bt, L, kv_scales=sc)
+        b.record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    rows = B * Sq
+    nbytes = rows * (1152 + 8 + (580 if fp8 else 1152))
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "KV-cache append GB/s", "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "u8" if fp8 else "bf16", "data": "synthetic",
+        "config": {"workload": args.workload, "op": "kv_append", "rows": rows,
+                   "kv": inp["kv_dtype"]},
+        "alg_bytes": nbytes,
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 6), "traffic": None,
+                     "kernel": "append_kernel", "kernel_ms": round(ms, 5),
+                     "note": "a few hundred KB per launch: launch latency, not bandwidth, bounds it"},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -123,6 +167,8 @@ def main():
     ap.add_argument("--graph", action="store_true", help="time HIP graph replays of the step")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run plain 1 GiB device copies (calibrates HBM byte counters)")
+    ap.add_argument("--op", default="decode", choices=["decode", "append"],
+                    help="decode: the decode step (default); append: the cache append alone")
     args = ap.parse_args()
     if args.copy_probe:
         # Known traffic: each copy reads and writes exactly 1 GiB.
@@ -137,6 +183,10 @@ def main():
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the path is single-GPU; sharding is described in DESIGN.md)", file=sys.stderr)
         sys.exit(2)
+
+    if args.op == "append":
+        bench_append(args)
+        return
 
     import mla_latent_kv_12_amd as mla
     dev = torch.device("cuda:0")

@@ -172,6 +172,31 @@ mla_status mla_combine(const int32_t *cache_seqlens, int B, int Sq, int H, int t
                        float *lse, void *workspace, size_t ws_bytes, int num_wg,
                        hipStream_t stream);
 
+/*
+ * Cache append of a decode step: writes the Sq new latent rows of every
+ * sequence into their cache slots, the step that precedes attention
+ * ("MLA & DSA 推理性能优化指南" §4, decode-flow figure: the output token is
+ * appended to the cache).  Row s of sequence b, new_kv[b, s, :] (bf16
+ * [B, Sq, 576], [c | k_rope]), goes to logical position j = L_b - Sq + s,
+ * i.e. to kv_pages[block_table[b, j / 64], j % 64, :], where
+ * L_b = cache_seqlens[b] already counts the new tokens (the convention of
+ * mla_decode).  Rows with j < 0, with j / 64 >= bt_stride or with a page entry
+ * outside [0, num_pages) are skipped.
+ *   bf16 cache: the row is copied bit for bit.
+ *   fp8 cache:  scale = max|x| / 448 over the row's 576 values (1 when all
+ *               are zero); code = e4m3fn round-to-nearest-even of x / scale
+ *               after clamping to +-448, computed in fp32 (correctly rounded
+ *               division); the scale goes to kv_scales[page, j % 64].  Rows
+ *               holding non-finite values get unspecified codes.
+ * Distinct (b, s) must map to distinct slots (the caller's page allocation);
+ * nothing else in the cache is written.
+ * Alignment: new_kv, kv_pages 16 B; kv_scales, block_table, cache_seqlens 4 B.
+ */
+mla_status mla_kv_append(const void *new_kv, void *kv_pages, float *kv_scales,
+                         mla_kv_dtype kv_dtype, int num_pages, const int32_t *block_table,
+                         int bt_stride, const int32_t *cache_seqlens, int B, int Sq,
+                         hipStream_t stream);
+
 /* Static name of a status code ("MLA_OK", ...). */
 const char *mla_status_str(mla_status s);
 

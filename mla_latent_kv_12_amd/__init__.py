@@ -9,6 +9,8 @@ or the tensors are not on a GPU, calls raise.
                       softmax_scale, kv_scales=None, causal=False)
     out, lse = sparse_decode(q_nope, q_rope, kv_pages, block_table,
                              cache_seqlens, indices, softmax_scale)
+    kv_append(new_kv, kv_pages, block_table, cache_seqlens, kv_scales=None)
+    idx = dsa_select(scores, cache_seqlens, n_select, n_init, n_local)
 """
 from __future__ import annotations
 
@@ -25,7 +27,7 @@ MLA_KV_FP8_E4M3 = 1
 STATUS = ["MLA_OK", "MLA_ERR_NULL", "MLA_ERR_SHAPE", "MLA_ERR_UNSUPPORTED", "MLA_ERR_ALIGN",
           "MLA_ERR_WORKSPACE", "MLA_ERR_HIP"]
 EXPORTS = ["mla_workspace_size", "mla_plan", "mla_decode", "mla_sparse_decode", "mla_attend",
-           "mla_combine", "mla_status_str", "mla_last_error"]
+           "mla_combine", "mla_kv_append", "mla_status_str", "mla_last_error"]
 
 _lib = None
 
@@ -61,6 +63,8 @@ def lib():
                                  f32, i32, vp, vp, vp, sz, i32, vp]
         L.mla_combine.restype = i32
         L.mla_combine.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, sz, i32, vp]
+        L.mla_kv_append.restype = i32
+        L.mla_kv_append.argtypes = [vp, vp, vp, i32, i32, vp, i32, vp, i32, i32, vp]
         L.mla_status_str.restype = ctypes.c_char_p
         L.mla_status_str.argtypes = [i32]
         L.mla_last_error.restype = ctypes.c_char_p
@@ -210,3 +214,30 @@ def combine(cache_seqlens, B, Sq, H, out, lse, workspace, topk=0, num_wg=0):
                              lse.data_ptr(), workspace.data_ptr(), workspace.numel(), int(num_wg),
                              _stream(out)))
     return out, lse
+
+
+def kv_append(new_kv, kv_pages, block_table, cache_seqlens, kv_scales=None):
+    """Write new_kv [B, Sq, 576] (bf16) into the cache slots of the Sq newest
+    tokens of every sequence (mla_kv_append); quantises for an fp8 cache."""
+    _req(new_kv, "new_kv", (torch.bfloat16,), 3)
+    B, Sq, d = new_kv.shape
+    if d != 576:
+        raise ValueError("new_kv must be [B, Sq, 576]")
+    _req(kv_pages, "kv_pages", (torch.bfloat16, torch.uint8, torch.float8_e4m3fn), 3)
+    if tuple(kv_pages.shape[1:]) != (64, 576):
+        raise ValueError("kv_pages must be [num_pages, 64, 576]")
+    fp8 = kv_pages.dtype != torch.bfloat16
+    if fp8:
+        if kv_scales is None:
+            raise ValueError("an fp8 cache needs kv_scales")
+        _req(kv_scales, "kv_scales", (torch.float32,), 2)
+        if tuple(kv_scales.shape) != (kv_pages.shape[0], 64):
+            raise ValueError("kv_scales must be [num_pages, 64]")
+    _req(block_table, "block_table", (torch.int32,), 2)
+    _req(cache_seqlens, "cache_seqlens", (torch.int32,), 1)
+    if block_table.shape[0] != B or cache_seqlens.shape[0] != B:
+        raise ValueError("block_table must be [B, max_pages] and cache_seqlens [B]")
+    _check(lib().mla_kv_append(
+        new_kv.data_ptr(), kv_pages.data_ptr(), kv_scales.data_ptr() if fp8 else None,
+        MLA_KV_FP8_E4M3 if fp8 else MLA_KV_BF16, kv_pages.shape[0], block_table.data_ptr(),
+        block_table.shape[1], cache_seqlens.data_ptr(), B, Sq, _stream(new_kv)))

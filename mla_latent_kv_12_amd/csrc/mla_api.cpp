@@ -267,6 +267,38 @@ mla_status mla_combine(const int32_t* cache_seqlens, int B, int Sq, int H, int t
   return MLA_OK;
 }
 
+mla_status mla_kv_append(const void* new_kv, void* kv_pages, float* kv_scales,
+                         mla_kv_dtype kv_dtype, int num_pages, const int32_t* block_table,
+                         int bt_stride, const int32_t* cache_seqlens, int B, int Sq,
+                         hipStream_t stream) {
+  g_err[0] = 0;
+  if (!new_kv || !kv_pages || !block_table || !cache_seqlens)
+    return fail(MLA_ERR_NULL, "a required tensor pointer is NULL");
+  if (kv_dtype != MLA_KV_BF16 && kv_dtype != MLA_KV_FP8_E4M3)
+    return fail(MLA_ERR_SHAPE, "unknown kv_dtype %d", (int)kv_dtype);
+  if (kv_dtype == MLA_KV_FP8_E4M3 && !kv_scales) return fail(MLA_ERR_NULL, "fp8 cache needs kv_scales");
+  if (B <= 0 || Sq <= 0) return fail(MLA_ERR_SHAPE, "B, Sq must be >= 1 (got %d, %d)", B, Sq);
+  if ((long long)B * Sq > (1LL << 30)) return fail(MLA_ERR_SHAPE, "B * Sq too large");
+  if (num_pages <= 0 || bt_stride <= 0)
+    return fail(MLA_ERR_SHAPE, "num_pages and bt_stride must be >= 1 (got %d, %d)", num_pages, bt_stride);
+  if (!aligned(new_kv, 16) || !aligned(kv_pages, 16) || (kv_scales && !aligned(kv_scales, 4)) ||
+      !aligned(block_table, 4) || !aligned(cache_seqlens, 4))
+    return fail(MLA_ERR_ALIGN, "tensor pointer misaligned (16 B for new_kv/kv, 4 B for the rest)");
+  mla::AppendArgs a;
+  a.src = static_cast<const uint16_t*>(new_kv);
+  a.kv = static_cast<uint8_t*>(kv_pages);
+  a.kv_scales = kv_scales;
+  a.block_table = block_table;
+  a.seqlens = cache_seqlens;
+  a.B = B;
+  a.Sq = Sq;
+  a.bt_stride = bt_stride;
+  a.num_pages = num_pages;
+  hipError_t e = mla::launch_append(a, kv_dtype == MLA_KV_FP8_E4M3, stream);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "append launch: %s", hipGetErrorString(e));
+  return MLA_OK;
+}
+
 const char* mla_status_str(mla_status s) {
   switch (s) {
     case MLA_OK: return "MLA_OK";

@@ -77,6 +77,17 @@ struct DecodeArgs {
   float scale_log2;  // softmax_scale * log2(e)
 };
 
+// Cache append: the Sq new latent rows of every sequence into their slots.
+struct AppendArgs {
+  const uint16_t* src;        // bf16 [B, Sq, 576]
+  uint8_t* kv;                // [num_pages, 64, 576] bf16 or e4m3fn
+  float* kv_scales;           // fp32 [num_pages, 64] (fp8 only)
+  const int32_t* block_table; // [B, bt_stride]
+  const int32_t* seqlens;     // [B], the new tokens included
+  int B, Sq, bt_stride, num_pages;
+};
+hipError_t launch_append(const AppendArgs& a, bool fp8, hipStream_t stream);
+
 hipError_t launch_plan(const Geometry& g, const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode(const Geometry& g, const DecodeArgs& a, bool fp8, hipStream_t stream);
 hipError_t launch_combine(const Geometry& g, const DecodeArgs& a, hipStream_t stream);

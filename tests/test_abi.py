@@ -114,3 +114,24 @@ def test_binding_refuses_cpu_tensors():
         mla.decode(q, torch.zeros(1, 1, 16, 64, dtype=torch.bfloat16),
                    torch.zeros(1, 64, 576, dtype=torch.bfloat16),
                    torch.zeros(1, 1, dtype=torch.int32), torch.ones(1, dtype=torch.int32), 0.1)
+
+
+def _append(**kw):
+    L = mla.lib()
+    a = dict(new=FAKE, kv=FAKE, scales=None, dtype=0, num_pages=10, bt=FAKE, bt_stride=4,
+             seqlens=FAKE, B=2, Sq=1)
+    a.update(kw)
+    return L.mla_kv_append(a["new"], a["kv"], a["scales"], a["dtype"], a["num_pages"], a["bt"],
+                           a["bt_stride"], a["seqlens"], a["B"], a["Sq"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(new=None), NULL), (dict(kv=None), NULL), (dict(bt=None), NULL), (dict(seqlens=None), NULL),
+    (dict(dtype=1), NULL),                                   # fp8 without scales
+    (dict(dtype=5), SHAPE), (dict(B=0), SHAPE), (dict(Sq=0), SHAPE), (dict(num_pages=0), SHAPE),
+    (dict(bt_stride=0), SHAPE), (dict(new=FAKE + 8), ALIGN), (dict(kv=FAKE + 4), ALIGN),
+    (dict(dtype=1, scales=FAKE + 2), ALIGN), (dict(seqlens=FAKE + 1), ALIGN),
+])
+def test_append_rejects_before_launch(kw, code):
+    assert _append(**kw) == code
+    assert mla.lib().mla_last_error().decode() != ""

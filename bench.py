@@ -155,6 +155,49 @@ def bench_append(args):
     }), flush=True)
 
 
+def bench_select(args):
+    """Times mla_dsa_select on the sparse workload's shape: one score per
+    64-token block of every query's context, 16 blocks selected (1 initial,
+    2 local).  Algorithmic bytes: the score rows read (4 B per block) and the
+    token lists written (4 B per listed token)."""
+    import mla_latent_kv_12_amd as mla
+    dev = torch.device("cuda:0")
+    cfg = S.config(args.workload if S.CONFIGS[args.workload]["topk"] > 0 else "dsa_sparse")
+    inp = S.make_inputs(dict(cfg, B=cfg["B"]), poison=False, unselected="nan")
+    B, Sq, topk = inp["B"], inp["Sq"], inp["topk"]
+    L = inp["cache_seqlens"].to(dev)
+    nbk = int(inp["block_table"].shape[1])
+    scores = torch.randn((B, Sq, nbk), generator=torch.Generator().manual_seed(98)).to(dev)
+    n_sel = topk // 64
+    idx = torch.empty((B, Sq, topk), dtype=torch.int32, device=dev)
+    for _ in range(args.warmup):
+        mla.dsa_select(scores, L, n_select=n_sel, indices=idx)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for a, b in evs:
+        a.record()
+        mla.dsa_select(scores, L, n_select=n_sel, indices=idx)
+        b.record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    nbytes = B * Sq * (nbk * 4 + topk * 4) + B * 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "DSA block top-k selection GB/s", "value": round(gbs, 2), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg["name"], "op": "dsa_select", "queries": B * Sq, "blocks": nbk,
+                   "n_select": n_sel},
+        "alg_bytes": nbytes,
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 6), "traffic": None,
+                     "kernel": "select_kernel", "kernel_ms": round(ms, 5),
+                     "note": "one workgroup per query, a few hundred KB in all: latency-bound"},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -167,8 +210,9 @@ def main():
     ap.add_argument("--graph", action="store_true", help="time HIP graph replays of the step")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run plain 1 GiB device copies (calibrates HBM byte counters)")
-    ap.add_argument("--op", default="decode", choices=["decode", "append"],
-                    help="decode: the decode step (default); append: the cache append alone")
+    ap.add_argument("--op", default="decode", choices=["decode", "append", "select"],
+                    help="decode: the decode step (default); append: the cache append alone; "
+                         "select: the DSA block top-k selection alone (sparse workloads)")
     args = ap.parse_args()
     if args.copy_probe:
         # Known traffic: each copy reads and writes exactly 1 GiB.
@@ -186,6 +230,9 @@ def main():
 
     if args.op == "append":
         bench_append(args)
+        return
+    if args.op == "select":
+        bench_select(args)
         return
 
     import mla_latent_kv_12_amd as mla

@@ -197,6 +197,30 @@ mla_status mla_kv_append(const void *new_kv, void *kv_pages, float *kv_scales,
                          int bt_stride, const int32_t *cache_seqlens, int B, int Sq,
                          hipStream_t stream);
 
+/*
+ * DSA block top-k selection: the token lists mla_sparse_decode consumes,
+ * from one indexer score per 64-token block ("MLA & DSA 推理性能优化指南"
+ * §1.2 figure: Lightning Indexer scores, GPU top-k selection, block-aligned
+ * k << L tokens; §6.1 table: 64-token blocks, 16 per query, 1 initial and
+ * 2 local blocks always selected).  The indexer itself is not part of this.
+ *   block_scores  fp32 [B, Sq, nbk]: score of block k (tokens 64k..64k+63)
+ *                 for query (b, s); NaN counts as -inf
+ *   cache_seqlens int32 [B], the Sq new tokens included
+ *   indices       int32 [B, Sq, n_select * 64] (written)
+ * Query s of sequence b sees L_s = L_b - Sq + s + 1 tokens (causal within
+ * the step), i.e. nb = min(ceil(L_s / 64), nbk) blocks.  If nb <= n_select
+ * every block is selected; otherwise blocks [0, n_init) and
+ * [nb - n_local, nb) are, plus the n_select - n_init - n_local blocks between
+ * them with the highest scores (ties: the lower block first).  The row lists
+ * the selected blocks' 64 token positions each, blocks in ascending order,
+ * with -1 for positions >= L_s and for unused slots.
+ * Limits: 1 <= nbk <= 16384; 1 <= n_select <= 256; n_init, n_local >= 0 with
+ * n_init + n_local <= n_select.  Alignment: 4 B.
+ */
+mla_status mla_dsa_select(const float *block_scores, int nbk, const int32_t *cache_seqlens, int B,
+                          int Sq, int n_select, int n_init, int n_local, int32_t *indices,
+                          hipStream_t stream);
+
 /* Static name of a status code ("MLA_OK", ...). */
 const char *mla_status_str(mla_status s);
 

@@ -10,7 +10,7 @@ or the tensors are not on a GPU, calls raise.
     out, lse = sparse_decode(q_nope, q_rope, kv_pages, block_table,
                              cache_seqlens, indices, softmax_scale)
     kv_append(new_kv, kv_pages, block_table, cache_seqlens, kv_scales=None)
-    idx = dsa_select(scores, cache_seqlens, n_select, n_init, n_local)
+    idx = dsa_select(block_scores, cache_seqlens, n_select=16, n_init=1, n_local=2)
 """
 from __future__ import annotations
 
@@ -27,7 +27,7 @@ MLA_KV_FP8_E4M3 = 1
 STATUS = ["MLA_OK", "MLA_ERR_NULL", "MLA_ERR_SHAPE", "MLA_ERR_UNSUPPORTED", "MLA_ERR_ALIGN",
           "MLA_ERR_WORKSPACE", "MLA_ERR_HIP"]
 EXPORTS = ["mla_workspace_size", "mla_plan", "mla_decode", "mla_sparse_decode", "mla_attend",
-           "mla_combine", "mla_kv_append", "mla_status_str", "mla_last_error"]
+           "mla_combine", "mla_kv_append", "mla_dsa_select", "mla_status_str", "mla_last_error"]
 
 _lib = None
 
@@ -65,6 +65,8 @@ def lib():
         L.mla_combine.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, sz, i32, vp]
         L.mla_kv_append.restype = i32
         L.mla_kv_append.argtypes = [vp, vp, vp, i32, i32, vp, i32, vp, i32, i32, vp]
+        L.mla_dsa_select.restype = i32
+        L.mla_dsa_select.argtypes = [vp, i32, vp, i32, i32, i32, i32, i32, vp, vp]
         L.mla_status_str.restype = ctypes.c_char_p
         L.mla_status_str.argtypes = [i32]
         L.mla_last_error.restype = ctypes.c_char_p
@@ -241,3 +243,22 @@ def kv_append(new_kv, kv_pages, block_table, cache_seqlens, kv_scales=None):
         new_kv.data_ptr(), kv_pages.data_ptr(), kv_scales.data_ptr() if fp8 else None,
         MLA_KV_FP8_E4M3 if fp8 else MLA_KV_BF16, kv_pages.shape[0], block_table.data_ptr(),
         block_table.shape[1], cache_seqlens.data_ptr(), B, Sq, _stream(new_kv)))
+
+
+def dsa_select(block_scores, cache_seqlens, n_select=16, n_init=1, n_local=2, indices=None):
+    """Token lists [B, Sq, n_select*64] (int32) for sparse_decode from block
+    scores [B, Sq, nbk] (fp32) (mla_dsa_select)."""
+    _req(block_scores, "block_scores", (torch.float32,), 3)
+    B, Sq, nbk = block_scores.shape
+    _req(cache_seqlens, "cache_seqlens", (torch.int32,), 1)
+    if cache_seqlens.shape[0] != B:
+        raise ValueError("cache_seqlens must be [B]")
+    if indices is None:
+        indices = torch.empty((B, Sq, n_select * 64), dtype=torch.int32, device=block_scores.device)
+    _req(indices, "indices", (torch.int32,), 3)
+    if tuple(indices.shape) != (B, Sq, n_select * 64):
+        raise ValueError("indices must be [B, Sq, n_select * 64]")
+    _check(lib().mla_dsa_select(block_scores.data_ptr(), nbk, cache_seqlens.data_ptr(), B, Sq,
+                                int(n_select), int(n_init), int(n_local), indices.data_ptr(),
+                                _stream(block_scores)))
+    return indices

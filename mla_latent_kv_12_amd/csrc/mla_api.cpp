@@ -299,6 +299,38 @@ mla_status mla_kv_append(const void* new_kv, void* kv_pages, float* kv_scales,
   return MLA_OK;
 }
 
+mla_status mla_dsa_select(const float* block_scores, int nbk, const int32_t* cache_seqlens, int B,
+                          int Sq, int n_select, int n_init, int n_local, int32_t* indices,
+                          hipStream_t stream) {
+  g_err[0] = 0;
+  if (!block_scores || !cache_seqlens || !indices)
+    return fail(MLA_ERR_NULL, "a required tensor pointer is NULL");
+  if (B <= 0 || Sq <= 0) return fail(MLA_ERR_SHAPE, "B, Sq must be >= 1 (got %d, %d)", B, Sq);
+  if ((long long)B * Sq > (1LL << 30)) return fail(MLA_ERR_SHAPE, "B * Sq too large");
+  if (nbk <= 0) return fail(MLA_ERR_SHAPE, "nbk must be >= 1 (got %d)", nbk);
+  if (nbk > mla::kMaxSelBlocks)
+    return fail(MLA_ERR_UNSUPPORTED, "nbk %d exceeds %d blocks per score row", nbk, mla::kMaxSelBlocks);
+  if (n_select <= 0 || n_select > mla::kMaxSelect)
+    return fail(MLA_ERR_SHAPE, "n_select must be in [1, %d] (got %d)", mla::kMaxSelect, n_select);
+  if (n_init < 0 || n_local < 0 || n_init + n_local > n_select)
+    return fail(MLA_ERR_SHAPE, "n_init, n_local must be >= 0 with n_init + n_local <= n_select");
+  if (!aligned(block_scores, 4) || !aligned(cache_seqlens, 4) || !aligned(indices, 4))
+    return fail(MLA_ERR_ALIGN, "tensor pointers must be 4-byte aligned");
+  mla::SelectArgs a;
+  a.scores = block_scores;
+  a.seqlens = cache_seqlens;
+  a.indices = indices;
+  a.B = B;
+  a.Sq = Sq;
+  a.nbk = nbk;
+  a.n_select = n_select;
+  a.n_init = n_init;
+  a.n_local = n_local;
+  hipError_t e = mla::launch_select(a, stream);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "select launch: %s", hipGetErrorString(e));
+  return MLA_OK;
+}
+
 const char* mla_status_str(mla_status s) {
   switch (s) {
     case MLA_OK: return "MLA_OK";

@@ -88,6 +88,17 @@ struct AppendArgs {
 };
 hipError_t launch_append(const AppendArgs& a, bool fp8, hipStream_t stream);
 
+// DSA block top-k selection from per-block indexer scores.
+constexpr int kMaxSelect = 256;       // selected blocks per query
+constexpr int kMaxSelBlocks = 16384;  // blocks per score row (keys in LDS)
+struct SelectArgs {
+  const float* scores;      // [B, Sq, nbk]
+  const int32_t* seqlens;   // [B], the new tokens included
+  int32_t* indices;         // [B, Sq, n_select * 64]
+  int B, Sq, nbk, n_select, n_init, n_local;
+};
+hipError_t launch_select(const SelectArgs& a, hipStream_t stream);
+
 hipError_t launch_plan(const Geometry& g, const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode(const Geometry& g, const DecodeArgs& a, bool fp8, hipStream_t stream);
 hipError_t launch_combine(const Geometry& g, const DecodeArgs& a, hipStream_t stream);

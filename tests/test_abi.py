@@ -135,3 +135,22 @@ def _append(**kw):
 def test_append_rejects_before_launch(kw, code):
     assert _append(**kw) == code
     assert mla.lib().mla_last_error().decode() != ""
+
+
+def _select(**kw):
+    L = mla.lib()
+    a = dict(sc=FAKE, nbk=100, sl=FAKE, B=2, Sq=1, n=16, i=1, l=2, out=FAKE)
+    a.update(kw)
+    return L.mla_dsa_select(a["sc"], a["nbk"], a["sl"], a["B"], a["Sq"], a["n"], a["i"], a["l"],
+                            a["out"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(sc=None), NULL), (dict(sl=None), NULL), (dict(out=None), NULL),
+    (dict(B=0), SHAPE), (dict(Sq=0), SHAPE), (dict(nbk=0), SHAPE), (dict(nbk=16385), UNSUP),
+    (dict(n=0), SHAPE), (dict(n=257), SHAPE), (dict(i=-1), SHAPE), (dict(i=10, l=7), SHAPE),
+    (dict(sc=FAKE + 2), ALIGN), (dict(out=FAKE + 1), ALIGN),
+])
+def test_select_rejects_before_launch(kw, code):
+    assert _select(**kw) == code
+    assert mla.lib().mla_last_error().decode() != ""

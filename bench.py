@@ -198,6 +198,49 @@ def bench_select(args):
     }), flush=True)
 
 
+def bench_proj(args):
+    """Times mla_absorb_query or mla_project_out for the workload's B*Sq query
+    rows and H heads (d_h = 128, d_c = 512), random N(0, 1/512) bf16 weights.
+    Algorithmic bytes: the weights (H*128*512*2) read once, the input rows
+    read and the output rows written; FLOP 2*M*H*128*512."""
+    import mla_latent_kv_12_amd as mla
+    dev = torch.device("cuda:0")
+    cfg = S.config(args.workload)
+    M, H = cfg["B"] * cfg["Sq"], cfg["H"]
+    gen = torch.Generator().manual_seed(97)
+    absorb = args.op == "absorb"
+    kin, kout = (128, 512) if absorb else (512, 128)
+    x = torch.randn((M, H, kin), generator=gen).to(torch.bfloat16).to(dev)
+    w = (torch.randn((H, kout, kin), generator=gen) * 512 ** -0.5).to(torch.bfloat16).to(dev)
+    out = torch.empty((M, H, kout), dtype=torch.bfloat16, device=dev)
+    f = mla.absorb_query if absorb else mla.project_out
+    for _ in range(args.warmup):
+        f(x, w, out=out)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for a, b in evs:
+        a.record()
+        f(x, w, out=out)
+        b.record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    nbytes = H * 128 * 512 * 2 + M * H * (kin + kout) * 2
+    flop = 2.0 * M * H * 128 * 512
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": f"MLA {'query absorption' if absorb else 'output projection'} GB/s", "value": round(gbs, 2),
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "op": args.op, "M": M, "H": H},
+        "alg_bytes": nbytes, "alg_flop": flop, "tflops": round(flop / (ms * 1e-3) / 1e12, 3),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 5), "traffic": None, "kernel": "head_gemm_kernel",
+                     "kernel_ms": round(ms, 5)},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -210,9 +253,10 @@ def main():
     ap.add_argument("--graph", action="store_true", help="time HIP graph replays of the step")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run plain 1 GiB device copies (calibrates HBM byte counters)")
-    ap.add_argument("--op", default="decode", choices=["decode", "append", "select"],
+    ap.add_argument("--op", default="decode", choices=["decode", "append", "select", "absorb", "project"],
                     help="decode: the decode step (default); append: the cache append alone; "
-                         "select: the DSA block top-k selection alone (sparse workloads)")
+                         "select: the DSA block top-k selection alone (sparse workloads); "
+                         "absorb / project: the W_UK query absorption / W_UV output projection")
     args = ap.parse_args()
     if args.copy_probe:
         # Known traffic: each copy reads and writes exactly 1 GiB.
@@ -233,6 +277,9 @@ def main():
         return
     if args.op == "select":
         bench_select(args)
+        return
+    if args.op in ("absorb", "project"):
+        bench_proj(args)
         return
 
     import mla_latent_kv_12_amd as mla

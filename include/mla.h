@@ -221,6 +221,30 @@ mla_status mla_dsa_select(const float *block_scores, int nbk, const int32_t *cac
                           int Sq, int n_select, int n_init, int n_local, int32_t *indices,
                           hipStream_t stream);
 
+/*
+ * Per-head projections on either side of the absorbed decode.  With W_UK
+ * absorbed into the query ("MLA 在极长上下文下的显存带宽突围", section on
+ * absorbing the matrices at run time: q~ = q^C W^UK) the decode works in the
+ * 512-dim latent space; W_UV brings its output back to the head dimension
+ * ("MLA & DSA 推理性能优化指南" §1.1 figure: W_UK, W_UV map d_c to
+ * d_h x n_h; §5.1: d_c = 512, d_h = 128).  M = B*Sq query rows, H heads.
+ *
+ * mla_absorb_query:  q_nope[m, h, n] = sum_k q_c[m, h, k] * w_uk_t[h, n, k]
+ *   q_c     bf16 [M, H, 128]  per-head query (no RoPE part)
+ *   w_uk_t  bf16 [H, 512, 128] W_UK stored transposed (w_uk_t[h, n, k] is
+ *           W_UK[h][k][n], the weight that maps latent dim n to head dim k)
+ *   q_nope  bf16 [M, H, 512]  written (fp32 accumulation, rounded to nearest)
+ * mla_project_out:   o[m, h, j] = sum_d w_uv[h, j, d] * out_latent[m, h, d]
+ *   out_latent bf16 [M, H, 512] (the decode's out)
+ *   w_uv    bf16 [H, 128, 512]
+ *   o       bf16 [M, H, 128]  written (fp32 accumulation, rounded to nearest)
+ * Limits: M >= 1, 1 <= H <= 65535.  Alignment: 16 B.
+ */
+mla_status mla_absorb_query(const void *q_c, const void *w_uk_t, void *q_nope, int M, int H,
+                            hipStream_t stream);
+mla_status mla_project_out(const void *out_latent, const void *w_uv, void *o, int M, int H,
+                           hipStream_t stream);
+
 /* Static name of a status code ("MLA_OK", ...). */
 const char *mla_status_str(mla_status s);
 

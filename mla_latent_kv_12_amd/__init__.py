@@ -11,6 +11,8 @@ or the tensors are not on a GPU, calls raise.
                              cache_seqlens, indices, softmax_scale)
     kv_append(new_kv, kv_pages, block_table, cache_seqlens, kv_scales=None)
     idx = dsa_select(block_scores, cache_seqlens, n_select=16, n_init=1, n_local=2)
+    q_nope = absorb_query(q_c, w_uk_t)          # [B, Sq, H, 128] -> [B, Sq, H, 512]
+    o = project_out(out, w_uv)                  # [B, Sq, H, 512] -> [B, Sq, H, 128]
 """
 from __future__ import annotations
 
@@ -27,7 +29,8 @@ MLA_KV_FP8_E4M3 = 1
 STATUS = ["MLA_OK", "MLA_ERR_NULL", "MLA_ERR_SHAPE", "MLA_ERR_UNSUPPORTED", "MLA_ERR_ALIGN",
           "MLA_ERR_WORKSPACE", "MLA_ERR_HIP"]
 EXPORTS = ["mla_workspace_size", "mla_plan", "mla_decode", "mla_sparse_decode", "mla_attend",
-           "mla_combine", "mla_kv_append", "mla_dsa_select", "mla_status_str", "mla_last_error"]
+           "mla_combine", "mla_kv_append", "mla_dsa_select", "mla_absorb_query", "mla_project_out",
+           "mla_status_str", "mla_last_error"]
 
 _lib = None
 
@@ -67,6 +70,9 @@ def lib():
         L.mla_kv_append.argtypes = [vp, vp, vp, i32, i32, vp, i32, vp, i32, i32, vp]
         L.mla_dsa_select.restype = i32
         L.mla_dsa_select.argtypes = [vp, i32, vp, i32, i32, i32, i32, i32, vp, vp]
+        for fn in (L.mla_absorb_query, L.mla_project_out):
+            fn.restype = i32
+            fn.argtypes = [vp, vp, vp, i32, i32, vp]
         L.mla_status_str.restype = ctypes.c_char_p
         L.mla_status_str.argtypes = [i32]
         L.mla_last_error.restype = ctypes.c_char_p
@@ -262,3 +268,32 @@ def dsa_select(block_scores, cache_seqlens, n_select=16, n_init=1, n_local=2, in
                                 int(n_select), int(n_init), int(n_local), indices.data_ptr(),
                                 _stream(block_scores)))
     return indices
+
+
+def _proj(x, w, kin, kout, absorb, out):
+    _req(x, "input", (torch.bfloat16,))
+    _req(w, "weight", (torch.bfloat16,), 3)
+    if x.dim() < 2 or x.shape[-1] != kin:
+        raise ValueError(f"input must be [..., H, {kin}]")
+    H = x.shape[-2]
+    M = x.numel() // (H * kin)
+    if tuple(w.shape) != (H, kout, kin):
+        raise ValueError(f"weight must be [H, {kout}, {kin}]")
+    if out is None:
+        out = torch.empty(tuple(x.shape[:-1]) + (kout,), dtype=torch.bfloat16, device=x.device)
+    _req(out, "out", (torch.bfloat16,))
+    if tuple(out.shape) != tuple(x.shape[:-1]) + (kout,):
+        raise ValueError("out has the wrong shape")
+    f = lib().mla_absorb_query if absorb else lib().mla_project_out
+    _check(f(x.data_ptr(), w.data_ptr(), out.data_ptr(), M, H, _stream(x)))
+    return out
+
+
+def absorb_query(q_c, w_uk_t, out=None):
+    """q_nope [..., H, 512] = q_c [..., H, 128] . W_UK (w_uk_t is [H, 512, 128]) (mla_absorb_query)."""
+    return _proj(q_c, w_uk_t, 128, 512, True, out)
+
+
+def project_out(out_latent, w_uv, out=None):
+    """o [..., H, 128] = W_UV . out_latent [..., H, 512] (w_uv is [H, 128, 512]) (mla_project_out)."""
+    return _proj(out_latent, w_uv, 512, 128, False, out)

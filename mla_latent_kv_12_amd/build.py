@@ -10,7 +10,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmla.so")
 SOURCES = [os.path.join(CSRC, "mla_kernels.hip"), os.path.join(CSRC, "mla_cache.hip"),
-           os.path.join(CSRC, "mla_select.hip"), os.path.join(CSRC, "mla_api.cpp")]
+           os.path.join(CSRC, "mla_select.hip"), os.path.join(CSRC, "mla_proj.hip"),
+           os.path.join(CSRC, "mla_api.cpp")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed-fp32 VALU forms are kept out of the generated code on purpose.

@@ -331,6 +331,37 @@ mla_status mla_dsa_select(const float* block_scores, int nbk, const int32_t* cac
   return MLA_OK;
 }
 
+namespace {
+mla_status run_proj(const void* act, const void* w, void* c, int M, int H, bool absorb,
+                    hipStream_t stream) {
+  g_err[0] = 0;
+  if (!act || !w || !c) return fail(MLA_ERR_NULL, "a required tensor pointer is NULL");
+  if (M <= 0 || H <= 0 || H > 65535) return fail(MLA_ERR_SHAPE, "need M >= 1 and 1 <= H <= 65535 (got %d, %d)", M, H);
+  if ((long long)M * H > (1LL << 31) / 512) return fail(MLA_ERR_SHAPE, "M * H too large");
+  if (!aligned(act, 16) || !aligned(w, 16) || !aligned(c, 16))
+    return fail(MLA_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+  mla::ProjArgs a;
+  a.a = static_cast<const uint16_t*>(act);
+  a.w = static_cast<const uint16_t*>(w);
+  a.c = static_cast<uint16_t*>(c);
+  a.M = M;
+  a.H = H;
+  hipError_t e = mla::launch_proj(a, absorb, stream);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "projection launch: %s", hipGetErrorString(e));
+  return MLA_OK;
+}
+}  // namespace
+
+mla_status mla_absorb_query(const void* q_c, const void* w_uk_t, void* q_nope, int M, int H,
+                            hipStream_t stream) {
+  return run_proj(q_c, w_uk_t, q_nope, M, H, true, stream);
+}
+
+mla_status mla_project_out(const void* out_latent, const void* w_uv, void* o, int M, int H,
+                           hipStream_t stream) {
+  return run_proj(out_latent, w_uv, o, M, H, false, stream);
+}
+
 const char* mla_status_str(mla_status s) {
   switch (s) {
     case MLA_OK: return "MLA_OK";

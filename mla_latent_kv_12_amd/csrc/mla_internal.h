@@ -99,6 +99,16 @@ struct SelectArgs {
 };
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream);
 
+// Per-head projections around the absorbed decode: C[m, h, :] = A[m, h, :] Bt[h]^T.
+constexpr int kDHead = 128;  // head dimension d_h
+struct ProjArgs {
+  const uint16_t* a;  // bf16 [M, H, K]
+  const uint16_t* w;  // bf16 [H, N, K]
+  uint16_t* c;        // bf16 [M, H, N]
+  int M, H;
+};
+hipError_t launch_proj(const ProjArgs& a, bool absorb, hipStream_t stream);
+
 hipError_t launch_plan(const Geometry& g, const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode(const Geometry& g, const DecodeArgs& a, bool fp8, hipStream_t stream);
 hipError_t launch_combine(const Geometry& g, const DecodeArgs& a, hipStream_t stream);

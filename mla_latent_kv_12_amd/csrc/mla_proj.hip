@@ -1,0 +1,84 @@
+// HIP kernels of the two per-head projections on either side of the
+// absorbed decode, written for gfx950.
+//
+// With W_UK absorbed into the query ("MLA 在极长上下文下的显存带宽突围",
+// section on absorbing the matrices at run time: q~ = q^C W^UK) the decode
+// attends in the 512-dim latent space, and its 512-dim output per head is
+// brought back to the head dimension by W_UV ("MLA & DSA 推理性能优化指南"
+// §1.1 figure: W_UK and W_UV map d_c to d_h x n_h; §5.1: d_c = 512,
+// d_h = 128, 128 heads):
+//   absorb:  q_nope[m, h, :]  = q_c[m, h, :] . W_UK[h]         (128 -> 512)
+//   project: o[m, h, :]       = W_UV[h] . out_latent[m, h, :]   (512 -> 128)
+// Both are, per head, C[m][n] = sum_k A[m][k] Bt[n][k] with the contraction
+// index contiguous in both operands: W_UK is kept as its transpose
+// [H, 512, 128] (a storage choice made once for static weights), W_UV as
+// [H, 128, 512].  A wave computes D^T = Bt A^T for 32 columns n of one head
+// over up to 128 rows m with bf16 MFMA 32x32x16 and fp32 accumulation; its
+// weight fragments stay in registers while it walks the row tiles, so every
+// weight byte is read from HBM once.
+#include "mla_internal.h"
+
+namespace mla {
+namespace kern {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kRowsPerBlock = 128;
+
+// K: contraction length, N: output columns per head.
+template <int K, int N>
+__global__ __launch_bounds__(256) void head_gemm_kernel(ProjArgs a) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int l32 = lane & 31, g = lane >> 5;
+  const int n0 = (blockIdx.x * 4 + wave) * 32;
+  const int h = blockIdx.y;
+  const int m_base = blockIdx.z * kRowsPerBlock;
+  const int H = a.H, M = a.M;
+  constexpr int KS = K / 16;
+  // weight fragments: row n0 + l32 of Bt[h], k = 16 ks + 8 g .. + 7
+  bf16x8 wf[KS];
+  const bf16x8* wrow = reinterpret_cast<const bf16x8*>(a.w + ((size_t)h * N + n0 + l32) * K + 8 * g);
+#pragma unroll
+  for (int ks = 0; ks < KS; ks++) wf[ks] = wrow[2 * ks];
+  for (int mt = 0; mt < kRowsPerBlock / 32; mt++) {
+    const int m0 = m_base + 32 * mt;
+    if (m0 >= M) break;
+    const int row = m0 + l32;
+    const bool ok = row < M;
+    const bf16x8* arow = reinterpret_cast<const bf16x8*>(a.a + ((size_t)(ok ? row : m0) * H + h) * K + 8 * g);
+    f32x16 acc = {};
+#pragma unroll
+    for (int ks = 0; ks < KS; ks++) {
+      const bf16x8 av = ok ? arow[2 * ks] : bf16x8{};
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[ks], av, acc, 0, 0, 0);
+    }
+    // lane holds column m = row, rows n = n0 + 8 q + 4 g + i (i < 4) of D^T
+    if (ok) {
+      __bf16* crow = reinterpret_cast<__bf16*>(a.c) + ((size_t)row * H + h) * N + n0 + 4 * g;
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        bf16x4 v = {(__bf16)acc[4 * q], (__bf16)acc[4 * q + 1], (__bf16)acc[4 * q + 2], (__bf16)acc[4 * q + 3]};
+        *reinterpret_cast<bf16x4*>(crow + 8 * q) = v;
+      }
+    }
+  }
+}
+
+}  // namespace
+}  // namespace kern
+
+hipError_t launch_proj(const ProjArgs& a, bool absorb, hipStream_t stream) {
+  const unsigned mblocks = (unsigned)((a.M + kern::kRowsPerBlock - 1) / kern::kRowsPerBlock);
+  if (absorb)  // K = 128, N = 512
+    hipLaunchKernelGGL((kern::head_gemm_kernel<kDHead, kDC>), dim3(kDC / 128, a.H, mblocks), dim3(256),
+                       0, stream, a);
+  else         // K = 512, N = 128
+    hipLaunchKernelGGL((kern::head_gemm_kernel<kDC, kDHead>), dim3(kDHead / 128, a.H, mblocks), dim3(256),
+                       0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -154,3 +154,14 @@ def _select(**kw):
 def test_select_rejects_before_launch(kw, code):
     assert _select(**kw) == code
     assert mla.lib().mla_last_error().decode() != ""
+
+
+@pytest.mark.parametrize("fn", ["mla_absorb_query", "mla_project_out"])
+@pytest.mark.parametrize("args,code", [
+    ((None, FAKE, FAKE, 4, 8), NULL), ((FAKE, None, FAKE, 4, 8), NULL), ((FAKE, FAKE, None, 4, 8), NULL),
+    ((FAKE, FAKE, FAKE, 0, 8), SHAPE), ((FAKE, FAKE, FAKE, 4, 0), SHAPE), ((FAKE, FAKE, FAKE, 4, 70000), SHAPE),
+    ((FAKE + 8, FAKE, FAKE, 4, 8), ALIGN), ((FAKE, FAKE, FAKE + 4, 4, 8), ALIGN),
+])
+def test_projections_reject_before_launch(fn, args, code):
+    assert getattr(mla.lib(), fn)(*args, None) == code
+    assert mla.lib().mla_last_error().decode() != ""

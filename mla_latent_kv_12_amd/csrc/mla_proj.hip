@@ -12,10 +12,10 @@
 // Both are, per head, C[m][n] = sum_k A[m][k] Bt[n][k] with the contraction
 // index contiguous in both operands: W_UK is kept as its transpose
 // [H, 512, 128] (a storage choice made once for static weights), W_UV as
-// [H, 128, 512].  A wave computes D^T = Bt A^T for 32 columns n of one head
-// over up to 128 rows m with bf16 MFMA 32x32x16 and fp32 accumulation; its
-// weight fragments stay in registers while it walks the row tiles, so every
-// weight byte is read from HBM once.
+// [H, 128, 512].  A workgroup computes D^T = Bt A^T for 32 columns n of one
+// head over up to 128 rows m with bf16 MFMA 32x32x16 and fp32 accumulation;
+// its weight fragments stay in registers while it walks the row tiles, so
+// every weight byte is read from HBM once.
 #include "mla_internal.h"
 
 namespace mla {
@@ -28,35 +28,56 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kRowsPerBlock = 128;
 
-// K: contraction length, N: output columns per head.
-template <int K, int N>
+// K: contraction length, N: output columns per head, SPLIT: waves that
+// share one 32-column tile, each taking 1/SPLIT of the contraction (their
+// partial tiles are summed through LDS).  A workgroup of 4 waves computes
+// 4/SPLIT tiles of 32 columns of one head for up to 128 rows.  The long
+// contraction (K = 512) is split 4 ways: four times the waves of one wave
+// per tile, and a quarter of the dependent load chain per wave.
+template <int K, int N, int SPLIT>
 __global__ __launch_bounds__(256) void head_gemm_kernel(ProjArgs a) {
+  __shared__ float red[SPLIT > 1 ? 3 : 1][16][64];  // partial tiles of the non-leading waves
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int l32 = lane & 31, g = lane >> 5;
-  const int n0 = (blockIdx.x * 4 + wave) * 32;
+  const int part = wave % SPLIT;               // which share of the contraction
+  const int n0 = (blockIdx.x * (4 / SPLIT) + wave / SPLIT) * 32;
   const int h = blockIdx.y;
   const int m_base = blockIdx.z * kRowsPerBlock;
   const int H = a.H, M = a.M;
-  constexpr int KS = K / 16;
-  // weight fragments: row n0 + l32 of Bt[h], k = 16 ks + 8 g .. + 7
+  constexpr int KW = K / SPLIT;
+  constexpr int KS = KW / 16;
+  const int k_off = part * KW;
+  // weight fragments: row n0 + l32 of Bt[h], k = k_off + 16 ks + 8 g .. + 7
   bf16x8 wf[KS];
-  const bf16x8* wrow = reinterpret_cast<const bf16x8*>(a.w + ((size_t)h * N + n0 + l32) * K + 8 * g);
+  const bf16x8* wrow = reinterpret_cast<const bf16x8*>(a.w + ((size_t)h * N + n0 + l32) * K + k_off + 8 * g);
 #pragma unroll
   for (int ks = 0; ks < KS; ks++) wf[ks] = wrow[2 * ks];
   for (int mt = 0; mt < kRowsPerBlock / 32; mt++) {
     const int m0 = m_base + 32 * mt;
-    if (m0 >= M) break;
+    if (m0 >= M) break;  // uniform over the workgroup
     const int row = m0 + l32;
     const bool ok = row < M;
-    const bf16x8* arow = reinterpret_cast<const bf16x8*>(a.a + ((size_t)(ok ? row : m0) * H + h) * K + 8 * g);
+    const bf16x8* arow =
+        reinterpret_cast<const bf16x8*>(a.a + ((size_t)(ok ? row : m0) * H + h) * K + k_off + 8 * g);
+    bf16x8 av[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ks++) av[ks] = ok ? arow[2 * ks] : bf16x8{};
     f32x16 acc = {};
 #pragma unroll
-    for (int ks = 0; ks < KS; ks++) {
-      const bf16x8 av = ok ? arow[2 * ks] : bf16x8{};
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[ks], av, acc, 0, 0, 0);
+    for (int ks = 0; ks < KS; ks++) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[ks], av[ks], acc, 0, 0, 0);
+    if constexpr (SPLIT > 1) {
+      if (part > 0) {
+#pragma unroll
+        for (int r = 0; r < 16; r++) red[part - 1][r][lane] = acc[r];
+      }
+      __syncthreads();
+      if (part == 0) {
+#pragma unroll
+        for (int r = 0; r < 16; r++) acc[r] += red[0][r][lane] + red[1][r][lane] + red[2][r][lane];
+      }
     }
     // lane holds column m = row, rows n = n0 + 8 q + 4 g + i (i < 4) of D^T
-    if (ok) {
+    if (part == 0 && ok) {
       __bf16* crow = reinterpret_cast<__bf16*>(a.c) + ((size_t)row * H + h) * N + n0 + 4 * g;
 #pragma unroll
       for (int q = 0; q < 4; q++) {
@@ -64,6 +85,7 @@ __global__ __launch_bounds__(256) void head_gemm_kernel(ProjArgs a) {
         *reinterpret_cast<bf16x4*>(crow + 8 * q) = v;
       }
     }
+    if constexpr (SPLIT > 1) __syncthreads();
   }
 }
 
@@ -73,10 +95,10 @@ __global__ __launch_bounds__(256) void head_gemm_kernel(ProjArgs a) {
 hipError_t launch_proj(const ProjArgs& a, bool absorb, hipStream_t stream) {
   const unsigned mblocks = (unsigned)((a.M + kern::kRowsPerBlock - 1) / kern::kRowsPerBlock);
   if (absorb)  // K = 128, N = 512
-    hipLaunchKernelGGL((kern::head_gemm_kernel<kDHead, kDC>), dim3(kDC / 128, a.H, mblocks), dim3(256),
+    hipLaunchKernelGGL((kern::head_gemm_kernel<kDHead, kDC, 1>), dim3(kDC / 128, a.H, mblocks), dim3(256),
                        0, stream, a);
   else         // K = 512, N = 128
-    hipLaunchKernelGGL((kern::head_gemm_kernel<kDC, kDHead>), dim3(kDHead / 128, a.H, mblocks), dim3(256),
+    hipLaunchKernelGGL((kern::head_gemm_kernel<kDC, kDHead, 4>), dim3(kDHead / 32, a.H, mblocks), dim3(256),
                        0, stream, a);
   return hipGetLastError();
 }

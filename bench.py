@@ -241,6 +241,47 @@ def bench_proj(args):
     }), flush=True)
 
 
+def bench_prefill(args):
+    """Times mla_prefill: causal MHA over decompressed per-head K/V, B=1,
+    T=--prefill-len, H=128, d_qk 192, d_v 128, bf16 N(0,1).  FLOP: each of
+    the T(T+1)/2 visible (query, key) pairs per head costs 2*192 (score) +
+    2*128 (output); MFMA-bound, against the dense bf16 peak."""
+    import mla_latent_kv_12_amd as mla
+    dev = torch.device("cuda:0")
+    B, T, H = 1, args.prefill_len, 128
+    gen = torch.Generator().manual_seed(96)
+    q = torch.randn((B, T, H, 192), generator=gen).to(torch.bfloat16).to(dev)
+    k = torch.randn((B, T, H, 192), generator=gen).to(torch.bfloat16).to(dev)
+    v = torch.randn((B, T, H, 128), generator=gen).to(torch.bfloat16).to(dev)
+    out = torch.empty((B, T, H, 128), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, T, H), dtype=torch.float32, device=dev)
+    scale = 1.0 / np.sqrt(192.0)
+    for _ in range(args.warmup):
+        mla.prefill(q, k, v, scale, out=out, lse=lse)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for a, b in evs:
+        a.record()
+        mla.prefill(q, k, v, scale, out=out, lse=lse)
+        b.record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    flop = B * H * (T * (T + 1) / 2) * 2 * (192 + 128)
+    tfs = flop / (ms * 1e-3) / 1e12
+    print(json.dumps({
+        "metric": "MLA non-absorbed prefill TFLOP/s", "value": round(tfs, 2), "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic", "config": {"workload": "prefill", "op": "prefill", "B": B, "T": T, "H": H,
+                                        "causal": True},
+        "alg_flop": flop,
+        "roofline": {"bound": "mfma", "achieved": round(tfs, 2), "peak": MFMA_BF16_PEAK_TFS,
+                     "unit": "TFLOP/s", "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4), "traffic": None,
+                     "kernel": "prefill_kernel", "kernel_ms": round(ms, 5)},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -253,10 +294,12 @@ def main():
     ap.add_argument("--graph", action="store_true", help="time HIP graph replays of the step")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run plain 1 GiB device copies (calibrates HBM byte counters)")
-    ap.add_argument("--op", default="decode", choices=["decode", "append", "select", "absorb", "project"],
+    ap.add_argument("--op", default="decode", choices=["decode", "append", "select", "absorb", "project", "prefill"],
                     help="decode: the decode step (default); append: the cache append alone; "
                          "select: the DSA block top-k selection alone (sparse workloads); "
-                         "absorb / project: the W_UK query absorption / W_UV output projection")
+                         "absorb / project: the W_UK query absorption / W_UV output projection; "
+                         "prefill: non-absorbed causal MHA, B=1, T=--prefill-len, H=128")
+    ap.add_argument("--prefill-len", type=int, default=4096)
     args = ap.parse_args()
     if args.copy_probe:
         # Known traffic: each copy reads and writes exactly 1 GiB.
@@ -280,6 +323,9 @@ def main():
         return
     if args.op in ("absorb", "project"):
         bench_proj(args)
+        return
+    if args.op == "prefill":
+        bench_prefill(args)
         return
 
     import mla_latent_kv_12_amd as mla

@@ -245,6 +245,23 @@ mla_status mla_absorb_query(const void *q_c, const void *w_uk_t, void *q_nope, i
 mla_status mla_project_out(const void *out_latent, const void *w_uv, void *o, int M, int H,
                            hipStream_t stream);
 
+/*
+ * Non-absorbed prefill: standard multi-head attention over K and V already
+ * decompressed from the latent ("MLA & DSA 推理性能优化指南" §3.1: in
+ * prefill c is decompressed into full K and V and a standard MHA kernel runs;
+ * §5.1: 128 heads, d_h = 128, d_rope = 64).  Per head the query and key are
+ * [nope (128) | rope (64)] and the value is 128 wide:
+ *   out[b,t,h,:] = sum_j softmax_j(scale * q[b,t,h,:] . k[b,j,h,:]) v[b,j,h,:]
+ *   lse[b,t,h]   = ln sum_j exp(scale * q[b,t,h,:] . k[b,j,h,:])   (natural log)
+ * over j <= t when causal != 0, else over all j < T.
+ *   q, k  bf16 [B, T, H, 192];  v bf16 [B, T, H, 128]
+ *   out   bf16 [B, T, H, 128];  lse fp32 [B, T, H]   (written)
+ * softmax_scale finite and > 0.  Limits: B, T >= 1; 1 <= H, B <= 65535.
+ * Alignment: q, k, v, out 16 B; lse 4 B.
+ */
+mla_status mla_prefill(const void *q, const void *k, const void *v, int B, int T, int H,
+                       float softmax_scale, int causal, void *out, float *lse, hipStream_t stream);
+
 /* Static name of a status code ("MLA_OK", ...). */
 const char *mla_status_str(mla_status s);
 

@@ -13,6 +13,7 @@ or the tensors are not on a GPU, calls raise.
     idx = dsa_select(block_scores, cache_seqlens, n_select=16, n_init=1, n_local=2)
     q_nope = absorb_query(q_c, w_uk_t)          # [B, Sq, H, 128] -> [B, Sq, H, 512]
     o = project_out(out, w_uv)                  # [B, Sq, H, 512] -> [B, Sq, H, 128]
+    out, lse = prefill(q, k, v, softmax_scale)  # non-absorbed MHA over decompressed K/V
 """
 from __future__ import annotations
 
@@ -30,7 +31,7 @@ STATUS = ["MLA_OK", "MLA_ERR_NULL", "MLA_ERR_SHAPE", "MLA_ERR_UNSUPPORTED", "MLA
           "MLA_ERR_WORKSPACE", "MLA_ERR_HIP"]
 EXPORTS = ["mla_workspace_size", "mla_plan", "mla_decode", "mla_sparse_decode", "mla_attend",
            "mla_combine", "mla_kv_append", "mla_dsa_select", "mla_absorb_query", "mla_project_out",
-           "mla_status_str", "mla_last_error"]
+           "mla_prefill", "mla_status_str", "mla_last_error"]
 
 _lib = None
 
@@ -73,6 +74,8 @@ def lib():
         for fn in (L.mla_absorb_query, L.mla_project_out):
             fn.restype = i32
             fn.argtypes = [vp, vp, vp, i32, i32, vp]
+        L.mla_prefill.restype = i32
+        L.mla_prefill.argtypes = [vp, vp, vp, i32, i32, i32, f32, i32, vp, vp, vp]
         L.mla_status_str.restype = ctypes.c_char_p
         L.mla_status_str.argtypes = [i32]
         L.mla_last_error.restype = ctypes.c_char_p
@@ -297,3 +300,23 @@ def absorb_query(q_c, w_uk_t, out=None):
 def project_out(out_latent, w_uv, out=None):
     """o [..., H, 128] = W_UV . out_latent [..., H, 512] (w_uv is [H, 128, 512]) (mla_project_out)."""
     return _proj(out_latent, w_uv, 512, 128, False, out)
+
+
+def prefill(q, k, v, softmax_scale, causal=True, out=None, lse=None):
+    """Non-absorbed MHA over per-head q, k [B,T,H,192] and v [B,T,H,128] (mla_prefill);
+    returns (out bf16 [B,T,H,128], lse fp32 [B,T,H])."""
+    _req(q, "q", (torch.bfloat16,), 4)
+    _req(k, "k", (torch.bfloat16,), 4)
+    _req(v, "v", (torch.bfloat16,), 4)
+    B, T, H, d = q.shape
+    if d != 192 or tuple(k.shape) != (B, T, H, 192) or tuple(v.shape) != (B, T, H, 128):
+        raise ValueError("q, k must be [B,T,H,192] and v [B,T,H,128]")
+    if out is None:
+        out = torch.empty((B, T, H, 128), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, T, H), dtype=torch.float32, device=q.device)
+    _req(out, "out", (torch.bfloat16,), 4)
+    _req(lse, "lse", (torch.float32,), 3)
+    _check(lib().mla_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, T, H, float(softmax_scale),
+                             int(bool(causal)), out.data_ptr(), lse.data_ptr(), _stream(q)))
+    return out, lse

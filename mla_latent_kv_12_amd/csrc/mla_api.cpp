@@ -362,6 +362,33 @@ mla_status mla_project_out(const void* out_latent, const void* w_uv, void* o, in
   return run_proj(out_latent, w_uv, o, M, H, false, stream);
 }
 
+mla_status mla_prefill(const void* q, const void* k, const void* v, int B, int T, int H,
+                       float softmax_scale, int causal, void* out, float* lse, hipStream_t stream) {
+  g_err[0] = 0;
+  if (!q || !k || !v || !out || !lse) return fail(MLA_ERR_NULL, "a required tensor pointer is NULL");
+  if (B <= 0 || T <= 0 || H <= 0 || H > 65535 || B > 65535)
+    return fail(MLA_ERR_SHAPE, "need B, T >= 1 and 1 <= H, B <= 65535 (got %d, %d, %d)", B, T, H);
+  if ((long long)B * T * H > (1LL << 31) / 192) return fail(MLA_ERR_SHAPE, "B * T * H too large");
+  if (!isfinite(softmax_scale) || !(softmax_scale > 0.f))
+    return fail(MLA_ERR_SHAPE, "softmax_scale must be finite and > 0");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(lse, 4))
+    return fail(MLA_ERR_ALIGN, "tensor pointer misaligned (16 B for q/k/v/out, 4 B for lse)");
+  mla::PrefillArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  a.B = B;
+  a.T = T;
+  a.H = H;
+  a.causal = causal ? 1 : 0;
+  a.scale = softmax_scale;
+  hipError_t e = mla::launch_prefill(a, stream);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
+  return MLA_OK;
+}
+
 const char* mla_status_str(mla_status s) {
   switch (s) {
     case MLA_OK: return "MLA_OK";

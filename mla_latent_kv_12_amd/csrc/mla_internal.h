@@ -109,6 +109,18 @@ struct ProjArgs {
 };
 hipError_t launch_proj(const ProjArgs& a, bool absorb, hipStream_t stream);
 
+// Non-absorbed prefill over decompressed per-head Q/K (192 dims) and V (128).
+struct PrefillArgs {
+  const uint16_t* q;  // bf16 [B, T, H, 192]
+  const uint16_t* k;  // bf16 [B, T, H, 192]
+  const uint16_t* v;  // bf16 [B, T, H, 128]
+  uint16_t* out;      // bf16 [B, T, H, 128]
+  float* lse;         // fp32 [B, T, H]
+  int B, T, H, causal;
+  float scale;
+};
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
 hipError_t launch_plan(const Geometry& g, const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode(const Geometry& g, const DecodeArgs& a, bool fp8, hipStream_t stream);
 hipError_t launch_combine(const Geometry& g, const DecodeArgs& a, hipStream_t stream);

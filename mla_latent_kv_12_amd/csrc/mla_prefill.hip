@@ -1,0 +1,166 @@
+// HIP kernel of the non-absorbed MLA prefill, written for gfx950.
+//
+// In prefill the latent is decompressed into per-head K and V and a standard
+// multi-head attention kernel runs over them ("MLA & DSA 推理性能优化指南"
+// §3.1; the non-absorbed path of the §1.1 figure); per head the key is
+// [W_UK c_t | k_rope_t] (128 + 64 dims, §5.1), the value W_UV c_t (128).
+// Given those per-head Q, K, V this kernel computes, per (b, h, t),
+//   out = sum_j softmax(scale q_t . k_j) v_j over j <= t (causal) or j < T,
+//   lse = ln sum_j exp(scale q_t . k_j).
+//
+// One workgroup per (128 query rows, head, sequence); wave w owns rows
+// 32w..32w+31 with their Q in registers.  K/V tiles of 32 tokens are staged in
+// LDS by the whole workgroup (K row-padded, V stored transposed so that the
+// P.V operand reads are contiguous).  Per tile and wave: S^T = K Q^T with bf16
+// MFMA 32x32x16 over 192 dims, an online softmax in the log2 domain, P
+// through a wave-private LDS buffer into the MFMA operand layout, and
+// O^T += V^T P^T (fp32 accumulation).  Tiles entirely above a wave's rows are
+// skipped under the causal rule.
+#include "mla_internal.h"
+
+namespace mla {
+namespace kern {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kDqk = 192, kDv = 128;
+constexpr int kRowsWg = 128, kTile = 32;
+constexpr int kKStride = 200;  // bf16 elements per K row in LDS (400 B, 16-byte aligned, padded)
+constexpr int kVStride = 40;   // bf16 elements per V^T row (32 tokens + pad)
+constexpr int kPStride = 40;   // bf16 elements per P row (32 tokens + pad)
+constexpr float kNegInf = -__builtin_inff();
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kLn2 = 0.693147180559945309f;
+
+__global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(16))) __bf16 k_lds[kTile * kKStride];
+  __shared__ __attribute__((aligned(16))) __bf16 vt_lds[kDv * kVStride];
+  __shared__ __attribute__((aligned(16))) __bf16 p_lds[4][32 * kPStride];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int l32 = lane & 31, g = lane >> 5;
+  const int t0 = blockIdx.x * kRowsWg;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int T = a.T, H = a.H;
+  const size_t seq = (size_t)b * T;
+  const int row = t0 + 32 * wave + l32;  // this lane's query position
+  const bool row_ok = row < T;
+
+  // Q of the wave's rows (B operand: row l32, dims 16 ks + 8 g .. + 7)
+  bf16x8 qf[kDqk / 16];
+  {
+    const bf16x8* qp = reinterpret_cast<const bf16x8*>(a.q + ((seq + (row_ok ? row : 0)) * H + h) * kDqk + 8 * g);
+#pragma unroll
+    for (int ks = 0; ks < kDqk / 16; ks++) qf[ks] = row_ok ? qp[2 * ks] : bf16x8{};
+  }
+  f32x16 o[kDv / 32];
+#pragma unroll
+  for (int d = 0; d < kDv / 32; d++) o[d] = f32x16{};
+  float m_run = kNegInf, l_run = 0.f;
+  const float c2 = a.scale * kLog2e;
+
+  const int last = a.causal ? min(T - 1, t0 + kRowsWg - 1) : T - 1;
+  const int n_tiles = last / kTile + 1;
+  const int wave_last = t0 + 32 * wave + 31;  // highest row of the wave
+  __bf16* pw = p_lds[wave];
+  for (int j = 0; j < n_tiles; j++) {
+    const int k0 = j * kTile;
+    __syncthreads();  // the previous tile is no longer read
+    // K tile: 32 tokens x 24 pieces of 8 dims; V tile transposed into V^T
+    for (int p = tid; p < kTile * (kDqk / 8); p += 256) {
+      const int tok = p / (kDqk / 8), pc = p % (kDqk / 8);
+      bf16x8 v = {};
+      if (k0 + tok < T) v = *reinterpret_cast<const bf16x8*>(a.k + ((seq + k0 + tok) * H + h) * kDqk + 8 * pc);
+      *reinterpret_cast<bf16x8*>(&k_lds[tok * kKStride + 8 * pc]) = v;
+    }
+    for (int p = tid; p < kTile * (kDv / 8); p += 256) {
+      const int tok = p / (kDv / 8), pc = p % (kDv / 8);
+      bf16x8 v = {};
+      if (k0 + tok < T) v = *reinterpret_cast<const bf16x8*>(a.v + ((seq + k0 + tok) * H + h) * kDv + 8 * pc);
+#pragma unroll
+      for (int i = 0; i < 8; i++) vt_lds[(8 * pc + i) * kVStride + tok] = v[i];
+    }
+    __syncthreads();
+    if (a.causal && k0 > wave_last) continue;  // the whole tile lies above this wave's rows
+
+    // S^T[token][row] = K Q^T over 192 dims; lane holds row l32 and tokens
+    // 8 (i / 4) + 4 g + i % 4
+    f32x16 s = {};
+#pragma unroll
+    for (int ks = 0; ks < kDqk / 16; ks++) {
+      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&k_lds[l32 * kKStride + 16 * ks + 8 * g]);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s, 0, 0, 0);
+    }
+    // mask, then the online softmax (max over unscaled scores: scale > 0)
+    float mloc = kNegInf;
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+      const int tok = k0 + 8 * (i / 4) + 4 * g + (i % 4);
+      const bool ok = row_ok && tok < T && (!a.causal || tok <= row);
+      s[i] = ok ? s[i] : kNegInf;
+      mloc = fmaxf(mloc, s[i]);
+    }
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+    const float m_new = fmaxf(m_run, mloc * c2);
+    const float muse = m_new == kNegInf ? 0.f : m_new;
+    const float alpha = m_run == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m_run - muse);
+    m_run = m_new;
+    float psum = 0.f;
+    bf16x4 pq[4];
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+      const float p = s[i] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c2, -muse));
+      psum += p;
+      pq[i / 4][i % 4] = (__bf16)p;
+    }
+    l_run = l_run * alpha + psum;
+#pragma unroll
+    for (int d = 0; d < kDv / 32; d++) o[d] *= alpha;
+    // P[row][token] to LDS, read back as the B operand: row l32, tokens
+    // 16 kk + 8 g .. + 7
+#pragma unroll
+    for (int q4 = 0; q4 < 4; q4++) *reinterpret_cast<bf16x4*>(&pw[l32 * kPStride + 8 * q4 + 4 * g]) = pq[q4];
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the wave's P stores have landed
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int kk = 0; kk < 2; kk++) {
+      const bf16x8 pf = *reinterpret_cast<const bf16x8*>(&pw[l32 * kPStride + 16 * kk + 8 * g]);
+#pragma unroll
+      for (int d = 0; d < kDv / 32; d++) {
+        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(&vt_lds[(32 * d + l32) * kVStride + 16 * kk + 8 * g]);
+        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, o[d], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();  // P is read before the next tile rewrites it
+  }
+
+  // O^T[dim][row]: lane holds row l32, dims 32 d + 8 (i / 4) + 4 g + i % 4
+  const float l = l_run + __shfl_xor(l_run, 32);
+  if (!row_ok) return;
+  const bool empty = !(l > 0.f);
+  const float inv = empty ? 0.f : 1.f / l;
+  __bf16* op = reinterpret_cast<__bf16*>(a.out) + ((seq + row) * H + h) * kDv + 4 * g;
+#pragma unroll
+  for (int d = 0; d < kDv / 32; d++) {
+#pragma unroll
+    for (int q4 = 0; q4 < 4; q4++) {
+      bf16x4 w = {(__bf16)(o[d][4 * q4] * inv), (__bf16)(o[d][4 * q4 + 1] * inv),
+                  (__bf16)(o[d][4 * q4 + 2] * inv), (__bf16)(o[d][4 * q4 + 3] * inv)};
+      *reinterpret_cast<bf16x4*>(op + 32 * d + 8 * q4) = w;
+    }
+  }
+  if (g == 0) a.lse[(seq + row) * H + h] = empty ? kNegInf : (m_run + __log2f(l)) * kLn2;
+}
+
+}  // namespace
+}  // namespace kern
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
+  const dim3 grid((unsigned)((a.T + kern::kRowsWg - 1) / kern::kRowsWg), (unsigned)a.H, (unsigned)a.B);
+  hipLaunchKernelGGL(kern::prefill_kernel, grid, dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -165,3 +165,19 @@ def test_select_rejects_before_launch(kw, code):
 def test_projections_reject_before_launch(fn, args, code):
     assert getattr(mla.lib(), fn)(*args, None) == code
     assert mla.lib().mla_last_error().decode() != ""
+
+
+@pytest.mark.parametrize("args,code", [
+    ((None, FAKE, FAKE, 1, 64, 8, 0.1, 1, FAKE, FAKE), NULL),
+    ((FAKE, FAKE, FAKE, 1, 64, 8, 0.1, 1, FAKE, None), NULL),
+    ((FAKE, FAKE, FAKE, 0, 64, 8, 0.1, 1, FAKE, FAKE), SHAPE),
+    ((FAKE, FAKE, FAKE, 1, 0, 8, 0.1, 1, FAKE, FAKE), SHAPE),
+    ((FAKE, FAKE, FAKE, 1, 64, 0, 0.1, 1, FAKE, FAKE), SHAPE),
+    ((FAKE, FAKE, FAKE, 1, 64, 8, 0.0, 1, FAKE, FAKE), SHAPE),
+    ((FAKE, FAKE, FAKE, 1, 64, 8, float("nan"), 1, FAKE, FAKE), SHAPE),
+    ((FAKE + 8, FAKE, FAKE, 1, 64, 8, 0.1, 1, FAKE, FAKE), ALIGN),
+    ((FAKE, FAKE, FAKE, 1, 64, 8, 0.1, 1, FAKE, FAKE + 2), ALIGN),
+])
+def test_prefill_rejects_before_launch(args, code):
+    assert mla.lib().mla_prefill(*args, None) == code
+    assert mla.lib().mla_last_error().decode() != ""

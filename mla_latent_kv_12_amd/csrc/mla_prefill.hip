@@ -35,7 +35,7 @@ constexpr float kNegInf = -__builtin_inff();
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kLn2 = 0.693147180559945309f;
 
-__global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) __bf16 k_lds[kTile * kKStride];
   __shared__ __attribute__((aligned(16))) __bf16 vt_lds[kDv * kVStride];
   __shared__ __attribute__((aligned(16))) __bf16 p_lds[4][32 * kPStride];
@@ -65,24 +65,44 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   const int n_tiles = last / kTile + 1;
   const int wave_last = t0 + 32 * wave + 31;  // highest row of the wave
   __bf16* pw = p_lds[wave];
+  // Tile loads: K as 32 tokens x 24 pieces of 8 dims (3 per thread); V as
+  // 16 pieces of 8 dims x 32 tokens (2 per thread, consecutive lanes on
+  // consecutive tokens, so that the transposing LDS stores of one dim hit
+  // consecutive banks).  The next tile's loads are in flight while the
+  // current tile is computed.
+  constexpr int kKPer = kTile * (kDqk / 8) / 256, kVPer = kTile * (kDv / 8) / 256;
+  bf16x8 kr[kKPer], vr[kVPer];
+  auto load_tile = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < kKPer; i++) {
+      const int p = tid + 256 * i, tok = p / (kDqk / 8), pc = p % (kDqk / 8);
+      kr[i] = k0 + tok < T ? *reinterpret_cast<const bf16x8*>(a.k + ((seq + k0 + tok) * H + h) * kDqk + 8 * pc)
+                           : bf16x8{};
+    }
+#pragma unroll
+    for (int i = 0; i < kVPer; i++) {
+      const int p = tid + 256 * i, tok = p % kTile, pc = p / kTile;
+      vr[i] = k0 + tok < T ? *reinterpret_cast<const bf16x8*>(a.v + ((seq + k0 + tok) * H + h) * kDv + 8 * pc)
+                           : bf16x8{};
+    }
+  };
+  load_tile(0);
   for (int j = 0; j < n_tiles; j++) {
     const int k0 = j * kTile;
     __syncthreads();  // the previous tile is no longer read
-    // K tile: 32 tokens x 24 pieces of 8 dims; V tile transposed into V^T
-    for (int p = tid; p < kTile * (kDqk / 8); p += 256) {
-      const int tok = p / (kDqk / 8), pc = p % (kDqk / 8);
-      bf16x8 v = {};
-      if (k0 + tok < T) v = *reinterpret_cast<const bf16x8*>(a.k + ((seq + k0 + tok) * H + h) * kDqk + 8 * pc);
-      *reinterpret_cast<bf16x8*>(&k_lds[tok * kKStride + 8 * pc]) = v;
-    }
-    for (int p = tid; p < kTile * (kDv / 8); p += 256) {
-      const int tok = p / (kDv / 8), pc = p % (kDv / 8);
-      bf16x8 v = {};
-      if (k0 + tok < T) v = *reinterpret_cast<const bf16x8*>(a.v + ((seq + k0 + tok) * H + h) * kDv + 8 * pc);
 #pragma unroll
-      for (int i = 0; i < 8; i++) vt_lds[(8 * pc + i) * kVStride + tok] = v[i];
+    for (int i = 0; i < kKPer; i++) {
+      const int p = tid + 256 * i, tok = p / (kDqk / 8), pc = p % (kDqk / 8);
+      *reinterpret_cast<bf16x8*>(&k_lds[tok * kKStride + 8 * pc]) = kr[i];
+    }
+#pragma unroll
+    for (int i = 0; i < kVPer; i++) {
+      const int p = tid + 256 * i, tok = p % kTile, pc = p / kTile;
+#pragma unroll
+      for (int e = 0; e < 8; e++) vt_lds[(8 * pc + e) * kVStride + tok] = vr[i][e];
     }
     __syncthreads();
+    if (j + 1 < n_tiles) load_tile(k0 + kTile);
     if (a.causal && k0 > wave_last) continue;  // the whole tile lies above this wave's rows
 
     // S^T[token][row] = K Q^T over 192 dims; lane holds row l32 and tokens

@@ -113,14 +113,21 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
       const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&k_lds[l32 * kKStride + 16 * ks + 8 * g]);
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s, 0, 0, 0);
     }
-    // mask, then the online softmax (max over unscaled scores: scale > 0)
+    // mask (only tiles that reach past T or above the wave's first row need
+    // it), then the online softmax (max over unscaled scores: scale > 0)
     float mloc = kNegInf;
+    const bool full = k0 + kTile <= T && (!a.causal || k0 + kTile - 1 <= t0 + 32 * wave) && t0 + 32 * wave + 31 < T;
+    if (full) {
 #pragma unroll
-    for (int i = 0; i < 16; i++) {
-      const int tok = k0 + 8 * (i / 4) + 4 * g + (i % 4);
-      const bool ok = row_ok && tok < T && (!a.causal || tok <= row);
-      s[i] = ok ? s[i] : kNegInf;
-      mloc = fmaxf(mloc, s[i]);
+      for (int i = 0; i < 16; i++) mloc = fmaxf(mloc, s[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; i++) {
+        const int tok = k0 + 8 * (i / 4) + 4 * g + (i % 4);
+        const bool ok = row_ok && tok < T && (!a.causal || tok <= row);
+        s[i] = ok ? s[i] : kNegInf;
+        mloc = fmaxf(mloc, s[i]);
+      }
     }
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
     const float m_new = fmaxf(m_run, mloc * c2);
@@ -136,8 +143,11 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
       pq[i / 4][i % 4] = (__bf16)p;
     }
     l_run = l_run * alpha + psum;
+    // O only needs rescaling when some row's maximum moved (alpha != 1)
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
 #pragma unroll
-    for (int d = 0; d < kDv / 32; d++) o[d] *= alpha;
+      for (int d = 0; d < kDv / 32; d++) o[d] *= alpha;
+    }
     // P[row][token] to LDS, read back as the B operand: row l32, tokens
     // 16 kk + 8 g .. + 7
 #pragma unroll

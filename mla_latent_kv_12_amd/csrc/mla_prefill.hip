@@ -41,7 +41,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) __bf16 p_lds[4][32 * kPStride];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, g = lane >> 5;
-  const int t0 = blockIdx.x * kRowsWg;
+  // the last query tiles see the most keys: dispatch them first
+  const int t0 = (gridDim.x - 1 - blockIdx.x) * kRowsWg;
   const int h = blockIdx.y, b = blockIdx.z;
   const int T = a.T, H = a.H;
   const size_t seq = (size_t)b * T;

@@ -8,8 +8,8 @@
 //   out = sum_j softmax(scale q_t . k_j) v_j over j <= t (causal) or j < T,
 //   lse = ln sum_j exp(scale q_t . k_j).
 //
-// One workgroup per (128 query rows, head, sequence); wave w owns rows
-// 32w..32w+31 with their Q in registers.  K/V tiles of 32 tokens are staged in
+// One workgroup per (256 query rows, head, sequence); wave w owns rows
+// 32w..32w+31 with their Q in registers.  K/V tiles of 64 tokens are staged in
 // LDS by the whole workgroup (K row-padded, V stored transposed so that the
 // P.V operand reads are contiguous).  Per tile and wave: S^T = K Q^T with bf16
 // MFMA 32x32x16 over 192 dims, an online softmax in the log2 domain, P
@@ -27,18 +27,18 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kDqk = 192, kDv = 128;
-constexpr int kRowsWg = 128, kTile = 32;
+constexpr int kWaves = 8, kRowsWg = 32 * kWaves, kTile = 64;
 constexpr int kKStride = 200;  // bf16 elements per K row in LDS (400 B, 16-byte aligned, padded)
-constexpr int kVStride = 40;   // bf16 elements per V^T row (32 tokens + pad)
-constexpr int kPStride = 40;   // bf16 elements per P row (32 tokens + pad)
+constexpr int kVStride = 72;   // bf16 elements per V^T row (64 tokens + pad)
+constexpr int kPStride = 72;   // bf16 elements per P row (64 tokens + pad)
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kLn2 = 0.693147180559945309f;
 
-__global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) __bf16 k_lds[kTile * kKStride];
   __shared__ __attribute__((aligned(16))) __bf16 vt_lds[kDv * kVStride];
-  __shared__ __attribute__((aligned(16))) __bf16 p_lds[4][32 * kPStride];
+  __shared__ __attribute__((aligned(16))) __bf16 p_lds[kWaves][32 * kPStride];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, g = lane >> 5;
   // the last query tiles see the most keys: dispatch them first
@@ -71,18 +71,19 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   // consecutive tokens, so that the transposing LDS stores of one dim hit
   // consecutive banks).  The next tile's loads are in flight while the
   // current tile is computed.
-  constexpr int kKPer = kTile * (kDqk / 8) / 256, kVPer = kTile * (kDv / 8) / 256;
+  constexpr int kThreads = 64 * kWaves;
+  constexpr int kKPer = kTile * (kDqk / 8) / kThreads, kVPer = kTile * (kDv / 8) / kThreads;
   bf16x8 kr[kKPer], vr[kVPer];
   auto load_tile = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < kKPer; i++) {
-      const int p = tid + 256 * i, tok = p / (kDqk / 8), pc = p % (kDqk / 8);
+      const int p = tid + kThreads * i, tok = p / (kDqk / 8), pc = p % (kDqk / 8);
       kr[i] = k0 + tok < T ? *reinterpret_cast<const bf16x8*>(a.k + ((seq + k0 + tok) * H + h) * kDqk + 8 * pc)
                            : bf16x8{};
     }
 #pragma unroll
     for (int i = 0; i < kVPer; i++) {
-      const int p = tid + 256 * i, tok = p % kTile, pc = p / kTile;
+      const int p = tid + kThreads * i, tok = p % kTile, pc = p / kTile;
       vr[i] = k0 + tok < T ? *reinterpret_cast<const bf16x8*>(a.v + ((seq + k0 + tok) * H + h) * kDv + 8 * pc)
                            : bf16x8{};
     }
@@ -93,12 +94,12 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     __syncthreads();  // the previous tile is no longer read
 #pragma unroll
     for (int i = 0; i < kKPer; i++) {
-      const int p = tid + 256 * i, tok = p / (kDqk / 8), pc = p % (kDqk / 8);
+      const int p = tid + kThreads * i, tok = p / (kDqk / 8), pc = p % (kDqk / 8);
       *reinterpret_cast<bf16x8*>(&k_lds[tok * kKStride + 8 * pc]) = kr[i];
     }
 #pragma unroll
     for (int i = 0; i < kVPer; i++) {
-      const int p = tid + 256 * i, tok = p % kTile, pc = p / kTile;
+      const int p = tid + kThreads * i, tok = p % kTile, pc = p / kTile;
 #pragma unroll
       for (int e = 0; e < 8; e++) vt_lds[(8 * pc + e) * kVStride + tok] = vr[i][e];
     }
@@ -106,28 +107,34 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     if (j + 1 < n_tiles) load_tile(k0 + kTile);
     if (a.causal && k0 > wave_last) continue;  // the whole tile lies above this wave's rows
 
-    // S^T[token][row] = K Q^T over 192 dims; lane holds row l32 and tokens
-    // 8 (i / 4) + 4 g + i % 4
-    f32x16 s = {};
+    // S^T[token][row] = K Q^T over 192 dims for the tile's two 32-token
+    // halves; lane holds row l32 and tokens 32 hf + 8 (i / 4) + 4 g + i % 4
+    f32x16 s2[2] = {f32x16{}, f32x16{}};
 #pragma unroll
     for (int ks = 0; ks < kDqk / 16; ks++) {
-      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&k_lds[l32 * kKStride + 16 * ks + 8 * g]);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s, 0, 0, 0);
+#pragma unroll
+      for (int hf = 0; hf < 2; hf++) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&k_lds[(32 * hf + l32) * kKStride + 16 * ks + 8 * g]);
+        s2[hf] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s2[hf], 0, 0, 0);
+      }
     }
     // mask (only tiles that reach past T or above the wave's first row need
     // it), then the online softmax (max over unscaled scores: scale > 0)
     float mloc = kNegInf;
     const bool full = k0 + kTile <= T && (!a.causal || k0 + kTile - 1 <= t0 + 32 * wave) && t0 + 32 * wave + 31 < T;
-    if (full) {
 #pragma unroll
-      for (int i = 0; i < 16; i++) mloc = fmaxf(mloc, s[i]);
-    } else {
+    for (int hf = 0; hf < 2; hf++) {
+      if (full) {
 #pragma unroll
-      for (int i = 0; i < 16; i++) {
-        const int tok = k0 + 8 * (i / 4) + 4 * g + (i % 4);
-        const bool ok = row_ok && tok < T && (!a.causal || tok <= row);
-        s[i] = ok ? s[i] : kNegInf;
-        mloc = fmaxf(mloc, s[i]);
+        for (int i = 0; i < 16; i++) mloc = fmaxf(mloc, s2[hf][i]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+          const int tok = k0 + 32 * hf + 8 * (i / 4) + 4 * g + (i % 4);
+          const bool ok = row_ok && tok < T && (!a.causal || tok <= row);
+          s2[hf][i] = ok ? s2[hf][i] : kNegInf;
+          mloc = fmaxf(mloc, s2[hf][i]);
+        }
       }
     }
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
@@ -136,12 +143,20 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     const float alpha = m_run == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m_run - muse);
     m_run = m_new;
     float psum = 0.f;
-    bf16x4 pq[4];
 #pragma unroll
-    for (int i = 0; i < 16; i++) {
-      const float p = s[i] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c2, -muse));
-      psum += p;
-      pq[i / 4][i % 4] = (__bf16)p;
+    for (int hf = 0; hf < 2; hf++) {
+      bf16x4 pq[4];
+#pragma unroll
+      for (int i = 0; i < 16; i++) {
+        const float x = s2[hf][i];
+        const float p = x == kNegInf ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(x, c2, -muse));
+        psum += p;
+        pq[i / 4][i % 4] = (__bf16)p;
+      }
+      // P[row][token] to LDS
+#pragma unroll
+      for (int q4 = 0; q4 < 4; q4++)
+        *reinterpret_cast<bf16x4*>(&pw[l32 * kPStride + 32 * hf + 8 * q4 + 4 * g]) = pq[q4];
     }
     l_run = l_run * alpha + psum;
     // O only needs rescaling when some row's maximum moved (alpha != 1)
@@ -149,14 +164,11 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
       for (int d = 0; d < kDv / 32; d++) o[d] *= alpha;
     }
-    // P[row][token] to LDS, read back as the B operand: row l32, tokens
-    // 16 kk + 8 g .. + 7
-#pragma unroll
-    for (int q4 = 0; q4 < 4; q4++) *reinterpret_cast<bf16x4*>(&pw[l32 * kPStride + 8 * q4 + 4 * g]) = pq[q4];
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the wave's P stores have landed
     __builtin_amdgcn_wave_barrier();
+    // read back as the B operand (row l32, tokens 16 kk + 8 g .. + 7)
 #pragma unroll
-    for (int kk = 0; kk < 2; kk++) {
+    for (int kk = 0; kk < kTile / 16; kk++) {
       const bf16x8 pf = *reinterpret_cast<const bf16x8*>(&pw[l32 * kPStride + 16 * kk + 8 * g]);
 #pragma unroll
       for (int d = 0; d < kDv / 32; d++) {
@@ -190,7 +202,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)((a.T + kern::kRowsWg - 1) / kern::kRowsWg), (unsigned)a.H, (unsigned)a.B);
-  hipLaunchKernelGGL(kern::prefill_kernel, grid, dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(kern::prefill_kernel, grid, dim3(64 * kern::kWaves), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -12,9 +12,9 @@
 // 32w..32w+31 with their Q in registers.  K/V tiles of 64 tokens are staged in
 // LDS by the whole workgroup (K row-padded, V stored transposed so that the
 // P.V operand reads are contiguous).  Per tile and wave: S^T = K Q^T with bf16
-// MFMA 32x32x16 over 192 dims, an online softmax in the log2 domain, P
-// through a wave-private LDS buffer into the MFMA operand layout, and
-// O^T += V^T P^T (fp32 accumulation).  Tiles entirely above a wave's rows are
+// MFMA 32x32x16 over 192 dims, an online softmax in the log2 domain, P moved
+// into the MFMA operand layout by lane swaps in registers, and O^T += V^T P^T
+// (fp32 accumulation).  Tiles entirely above a wave's rows are
 // skipped under the causal rule.
 #include "mla_internal.h"
 
@@ -24,13 +24,14 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kDqk = 192, kDv = 128;
 constexpr int kWaves = 8, kRowsWg = 32 * kWaves, kTile = 64;
 constexpr int kKStride = 200;  // bf16 elements per K row in LDS (400 B, 16-byte aligned, padded)
 constexpr int kVStride = 72;   // bf16 elements per V^T row (64 tokens + pad)
-constexpr int kPStride = 72;   // bf16 elements per P row (64 tokens + pad)
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kLn2 = 0.693147180559945309f;
@@ -38,7 +39,6 @@ constexpr float kLn2 = 0.693147180559945309f;
 __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) __bf16 k_lds[kTile * kKStride];
   __shared__ __attribute__((aligned(16))) __bf16 vt_lds[kDv * kVStride];
-  __shared__ __attribute__((aligned(16))) __bf16 p_lds[kWaves][32 * kPStride];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, g = lane >> 5;
   // the last query tiles see the most keys: dispatch them first
@@ -65,7 +65,6 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) 
   const int last = a.causal ? min(T - 1, t0 + kRowsWg - 1) : T - 1;
   const int n_tiles = last / kTile + 1;
   const int wave_last = t0 + 32 * wave + 31;  // highest row of the wave
-  __bf16* pw = p_lds[wave];
   // Tile loads: K as 32 tokens x 24 pieces of 8 dims (3 per thread); V as
   // 16 pieces of 8 dims x 32 tokens (2 per thread, consecutive lanes on
   // consecutive tokens, so that the transposing LDS stores of one dim hit
@@ -142,21 +141,37 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) 
     const float muse = m_new == kNegInf ? 0.f : m_new;
     const float alpha = m_run == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m_run - muse);
     m_run = m_new;
+    // P in the operand layout of O^T += V^T P^T without a trip through LDS:
+    // for tokens 16 kk .. 16 kk + 15 lane (l32, g) holds, per half g, 4 of
+    // the 8 tokens its operand needs; swapping the second group of the lower
+    // lanes with the first group of the upper lanes (v_permlane32_swap)
+    // gives every lane its 8 consecutive tokens 16 kk + 8 g .. + 7.
     float psum = 0.f;
+    bf16x8 pf[kTile / 16];
 #pragma unroll
     for (int hf = 0; hf < 2; hf++) {
-      bf16x4 pq[4];
+      float pv[16];
 #pragma unroll
       for (int i = 0; i < 16; i++) {
         const float x = s2[hf][i];
-        const float p = x == kNegInf ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(x, c2, -muse));
-        psum += p;
-        pq[i / 4][i % 4] = (__bf16)p;
+        pv[i] = x == kNegInf ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(x, c2, -muse));
+        psum += pv[i];
       }
-      // P[row][token] to LDS
 #pragma unroll
-      for (int q4 = 0; q4 < 4; q4++)
-        *reinterpret_cast<bf16x4*>(&pw[l32 * kPStride + 32 * hf + 8 * q4 + 4 * g]) = pq[q4];
+      for (int h2 = 0; h2 < 2; h2++) {  // tokens 32 hf + 16 h2 .. + 15
+        unsigned xw[2], yw[2];
+#pragma unroll
+        for (int e = 0; e < 2; e++) {
+          bf16x2 xa = {(__bf16)pv[8 * h2 + 2 * e], (__bf16)pv[8 * h2 + 2 * e + 1]};
+          bf16x2 ya = {(__bf16)pv[8 * h2 + 4 + 2 * e], (__bf16)pv[8 * h2 + 4 + 2 * e + 1]};
+          const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, xa),
+                                                          __builtin_bit_cast(unsigned, ya), false, false);
+          xw[e] = r[0];
+          yw[e] = r[1];
+        }
+        u32x4 w = {xw[0], xw[1], yw[0], yw[1]};
+        pf[2 * hf + h2] = __builtin_bit_cast(bf16x8, w);
+      }
     }
     l_run = l_run * alpha + psum;
     // O only needs rescaling when some row's maximum moved (alpha != 1)
@@ -164,19 +179,14 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) 
 #pragma unroll
       for (int d = 0; d < kDv / 32; d++) o[d] *= alpha;
     }
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the wave's P stores have landed
-    __builtin_amdgcn_wave_barrier();
-    // read back as the B operand (row l32, tokens 16 kk + 8 g .. + 7)
 #pragma unroll
     for (int kk = 0; kk < kTile / 16; kk++) {
-      const bf16x8 pf = *reinterpret_cast<const bf16x8*>(&pw[l32 * kPStride + 16 * kk + 8 * g]);
 #pragma unroll
       for (int d = 0; d < kDv / 32; d++) {
         const bf16x8 vf = *reinterpret_cast<const bf16x8*>(&vt_lds[(32 * d + l32) * kVStride + 16 * kk + 8 * g]);
-        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, o[d], 0, 0, 0);
+        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kk], o[d], 0, 0, 0);
       }
     }
-    __builtin_amdgcn_wave_barrier();  // P is read before the next tile rewrites it
   }
 
   // O^T[dim][row]: lane holds row l32, dims 32 d + 8 (i / 4) + 4 g + i % 4

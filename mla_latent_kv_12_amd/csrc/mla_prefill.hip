@@ -37,8 +37,9 @@ constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kLn2 = 0.693147180559945309f;
 
 __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) __bf16 k_lds[kTile * kKStride];
-  __shared__ __attribute__((aligned(16))) __bf16 vt_lds[kDv * kVStride];
+  // two buffers: tile j + 1 is stored while tile j is read
+  __shared__ __attribute__((aligned(16))) __bf16 k_lds2[2][kTile * kKStride];
+  __shared__ __attribute__((aligned(16))) __bf16 vt_lds2[2][kDv * kVStride];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, g = lane >> 5;
   // the last query tiles see the most keys: dispatch them first
@@ -65,14 +66,18 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) 
   const int last = a.causal ? min(T - 1, t0 + kRowsWg - 1) : T - 1;
   const int n_tiles = last / kTile + 1;
   const int wave_last = t0 + 32 * wave + 31;  // highest row of the wave
-  // Tile loads: K as 32 tokens x 24 pieces of 8 dims (3 per thread); V as
-  // 16 pieces of 8 dims x 32 tokens (2 per thread, consecutive lanes on
-  // consecutive tokens, so that the transposing LDS stores of one dim hit
-  // consecutive banks).  The next tile's loads are in flight while the
-  // current tile is computed.
+  // Tile loads: K as 64 tokens x 24 pieces of 8 dims (3 per thread); V as
+  // 16 pieces of 8 dims x 64 tokens, a thread taking two consecutive tokens
+  // of one piece (2 per thread), so that the transposing LDS stores write
+  // both tokens of a dim as one 4-byte word and consecutive lanes hit
+  // consecutive banks.  Tile j + 1 is loaded into registers while tile j is
+  // computed and stored into the other LDS buffer afterwards: one workgroup
+  // barrier per tile.
   constexpr int kThreads = 64 * kWaves;
-  constexpr int kKPer = kTile * (kDqk / 8) / kThreads, kVPer = kTile * (kDv / 8) / kThreads;
+  constexpr int kKPer = kTile * (kDqk / 8) / kThreads, kVPer = 2;
+  static_assert(kTile * (kDv / 8) == kVPer * kThreads, "V tile split");
   bf16x8 kr[kKPer], vr[kVPer];
+  const int v_tok = 2 * (tid % 32), v_pc = tid / 32;
   auto load_tile = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < kKPer; i++) {
@@ -82,29 +87,33 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) 
     }
 #pragma unroll
     for (int i = 0; i < kVPer; i++) {
-      const int p = tid + kThreads * i, tok = p % kTile, pc = p / kTile;
-      vr[i] = k0 + tok < T ? *reinterpret_cast<const bf16x8*>(a.v + ((seq + k0 + tok) * H + h) * kDv + 8 * pc)
+      const int tok = v_tok + i;
+      vr[i] = k0 + tok < T ? *reinterpret_cast<const bf16x8*>(a.v + ((seq + k0 + tok) * H + h) * kDv + 8 * v_pc)
                            : bf16x8{};
     }
   };
-  load_tile(0);
-  for (int j = 0; j < n_tiles; j++) {
-    const int k0 = j * kTile;
-    __syncthreads();  // the previous tile is no longer read
+  auto store_tile = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < kKPer; i++) {
       const int p = tid + kThreads * i, tok = p / (kDqk / 8), pc = p % (kDqk / 8);
-      *reinterpret_cast<bf16x8*>(&k_lds[tok * kKStride + 8 * pc]) = kr[i];
+      *reinterpret_cast<bf16x8*>(&k_lds2[buf][tok * kKStride + 8 * pc]) = kr[i];
     }
 #pragma unroll
-    for (int i = 0; i < kVPer; i++) {
-      const int p = tid + kThreads * i, tok = p % kTile, pc = p / kTile;
-#pragma unroll
-      for (int e = 0; e < 8; e++) vt_lds[(8 * pc + e) * kVStride + tok] = vr[i][e];
+    for (int e = 0; e < 8; e++) {
+      bf16x2 w = {vr[0][e], vr[1][e]};
+      *reinterpret_cast<bf16x2*>(&vt_lds2[buf][(8 * v_pc + e) * kVStride + v_tok]) = w;
     }
-    __syncthreads();
-    if (j + 1 < n_tiles) load_tile(k0 + kTile);
-    if (a.causal && k0 > wave_last) continue;  // the whole tile lies above this wave's rows
+  };
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+  for (int j = 0; j < n_tiles; j++) {
+    const int k0 = j * kTile;
+    const __bf16* k_lds = k_lds2[j & 1];
+    const __bf16* vt_lds = vt_lds2[j & 1];
+    const bool more = j + 1 < n_tiles;
+    if (more) load_tile(k0 + kTile);
+    if (!(a.causal && k0 > wave_last)) {  // else the whole tile lies above this wave's rows
 
     // S^T[token][row] = K Q^T over 192 dims for the tile's two 32-token
     // halves; lane holds row l32 and tokens 32 hf + 8 (i / 4) + 4 g + i % 4
@@ -187,6 +196,9 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) 
         o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kk], o[d], 0, 0, 0);
       }
     }
+    }
+    if (more) store_tile((j + 1) & 1);  // the other buffer: last read before the previous barrier
+    __syncthreads();
   }
 
   // O^T[dim][row]: lane holds row l32, dims 32 d + 8 (i / 4) + 4 g + i % 4

@@ -18,6 +18,8 @@
 // skipped under the causal rule.
 #include "mla_internal.h"
 
+#include <utility>
+
 namespace mla {
 namespace kern {
 namespace {
@@ -35,6 +37,27 @@ constexpr int kVStride = 72;   // bf16 elements per V^T row (64 tokens + pad)
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kLn2 = 0.693147180559945309f;
+
+// K operand reads issued from assembly with explicit counted waits, so that
+// several are in flight per MFMA (the compiler keeps about two).  At the
+// start of a tile's scores no other LDS operation of the wave is pending
+// (the workgroup barrier drained them), so the counts are exact.
+template <int OFF>
+__device__ __forceinline__ void lds_rd16(bf16x8& dst, uint32_t addr) {
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(dst) : "v"(addr), "n"(OFF));
+}
+template <int N>
+__device__ __forceinline__ void lds_ready(bf16x8& v) {
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(v) : "n"(N));
+}
+template <typename F, int... I>
+__device__ __forceinline__ void unroll_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void unroll(F&& f) {
+  unroll_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) {
   // two buffers: tile j + 1 is stored while tile j is read
@@ -117,14 +140,25 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) 
 
     // S^T[token][row] = K Q^T over 192 dims for the tile's two 32-token
     // halves; lane holds row l32 and tokens 32 hf + 8 (i / 4) + 4 g + i % 4
+    // operand n = 2 ks + hf: token 32 hf + l32, dims 16 ks + 8 g .. + 7
     f32x16 s2[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-    for (int ks = 0; ks < kDqk / 16; ks++) {
-#pragma unroll
-      for (int hf = 0; hf < 2; hf++) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&k_lds[(32 * hf + l32) * kKStride + 16 * ks + 8 * g]);
-        s2[hf] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s2[hf], 0, 0, 0);
-      }
+    {
+      constexpr int kN = 2 * (kDqk / 16), kLead = 4, kRing = 6;
+      const uint32_t kb = (uint32_t)reinterpret_cast<uintptr_t>(k_lds);
+      const uint32_t ad[2] = {kb + (uint32_t)((l32 * kKStride + 8 * g) * 2),
+                              kb + (uint32_t)(((32 + l32) * kKStride + 8 * g) * 2)};
+      bf16x8 ring[kRing];
+      auto rd = [&](auto NI) {
+        constexpr int n = decltype(NI)::value;
+        lds_rd16<32 * (n / 2)>(ring[n % kRing], ad[n % 2]);
+      };
+      unroll<kLead>(rd);
+      unroll<kN>([&](auto NI) {
+        constexpr int n = decltype(NI)::value;
+        lds_ready<(kLead - 1 < kN - 1 - n ? kLead - 1 : kN - 1 - n)>(ring[n % kRing]);
+        s2[n % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[n % kRing], qf[n / 2], s2[n % 2], 0, 0, 0);
+        if constexpr (n + kLead < kN) rd(std::integral_constant<int, n + kLead>{});
+      });
     }
     // mask (only tiles that reach past T or above the wave's first row need
     // it), then the online softmax (max over unscaled scores: scale > 0)

@@ -60,9 +60,10 @@ __device__ __forceinline__ void unroll(F&& f) {
 }
 
 __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) {
-  // two buffers: tile j + 1 is stored while tile j is read
-  __shared__ __attribute__((aligned(16))) __bf16 k_lds2[2][kTile * kKStride];
-  __shared__ __attribute__((aligned(16))) __bf16 vt_lds2[2][kDv * kVStride];
+  // three buffers: tile j + 1 is stored while tile j (scores) and tile
+  // j - 1 (its P.V, pipelined into step j) are read
+  __shared__ __attribute__((aligned(16))) __bf16 k_lds2[3][kTile * kKStride];
+  __shared__ __attribute__((aligned(16))) __bf16 vt_lds2[3][kDv * kVStride];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, g = lane >> 5;
   // the last query tiles see the most keys: dispatch them first
@@ -127,16 +128,50 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) 
       *reinterpret_cast<bf16x2*>(&vt_lds2[buf][(8 * v_pc + e) * kVStride + v_tok]) = w;
     }
   };
+  // P.V of tile j - 1 runs in step j beside tile j's softmax.  Before the
+  // first tile it runs on a zeroed V buffer with P = 0 (adds nothing), so
+  // the common step has no branch between the two.
+  bf16x8 pf_prev[kTile / 16];
+#pragma unroll
+  for (int kk = 0; kk < kTile / 16; kk++) pf_prev[kk] = bf16x8{};
+  float alpha_prev = 1.f;
+  bool pend = false;
+  for (int i = tid; i < kDv * kVStride / 2; i += kThreads) reinterpret_cast<unsigned*>(vt_lds2[2])[i] = 0u;
+  auto pv_step = [&](const __bf16* vt) {
+#pragma unroll
+    for (int kk = 0; kk < kTile / 16; kk++) {
+#pragma unroll
+      for (int d = 0; d < kDv / 32; d++) {
+        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(&vt[(32 * d + l32) * kVStride + 16 * kk + 8 * g]);
+        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf_prev[kk], o[d], 0, 0, 0);
+      }
+    }
+  };
+  auto rescale_prev = [&]() {  // O only needs rescaling when some row's maximum moved
+    if (__builtin_amdgcn_ballot_w64(alpha_prev != 1.f) != 0) {
+#pragma unroll
+      for (int d = 0; d < kDv / 32; d++) o[d] *= alpha_prev;
+    }
+  };
   load_tile(0);
   store_tile(0);
   __syncthreads();
+  int cur = 0;  // buffer of tile j; tile j - 1 is in (cur + 2) % 3
   for (int j = 0; j < n_tiles; j++) {
     const int k0 = j * kTile;
-    const __bf16* k_lds = k_lds2[j & 1];
-    const __bf16* vt_lds = vt_lds2[j & 1];
+    const int prv = cur == 0 ? 2 : cur - 1, nxt = cur == 2 ? 0 : cur + 1;
+    const __bf16* k_lds = k_lds2[cur];
     const bool more = j + 1 < n_tiles;
     if (more) load_tile(k0 + kTile);
-    if (!(a.causal && k0 > wave_last)) {  // else the whole tile lies above this wave's rows
+    if (a.causal && k0 > wave_last) {
+      // the whole tile lies above this wave's rows: only finish the last
+      // computed tile's P.V (once)
+      if (pend) {
+        rescale_prev();
+        pv_step(vt_lds2[prv]);
+        pend = false;
+      }
+    } else {
 
     // S^T[token][row] = K Q^T over 192 dims for the tile's two 32-token
     // halves; lane holds row l32 and tokens 32 hf + 8 (i / 4) + 4 g + i % 4
@@ -160,6 +195,9 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) 
         if constexpr (n + kLead < kN) rd(std::integral_constant<int, n + kLead>{});
       });
     }
+    // rescale O for tile j - 1's maximum before its P.V (a branch, kept out
+    // of the block where that P.V interleaves with this tile's softmax)
+    rescale_prev();
     // mask (only tiles that reach past T or above the wave's first row need
     // it), then the online softmax (max over unscaled scores: scale > 0)
     float mloc = kNegInf;
@@ -217,22 +255,21 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) 
       }
     }
     l_run = l_run * alpha + psum;
-    // O only needs rescaling when some row's maximum moved (alpha != 1)
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
+    pv_step(vt_lds2[prv]);  // tile j - 1 (or nothing before the first tile)
 #pragma unroll
-      for (int d = 0; d < kDv / 32; d++) o[d] *= alpha;
+    for (int kk = 0; kk < kTile / 16; kk++) pf_prev[kk] = pf[kk];
+    alpha_prev = alpha;
+    pend = true;
     }
-#pragma unroll
-    for (int kk = 0; kk < kTile / 16; kk++) {
-#pragma unroll
-      for (int d = 0; d < kDv / 32; d++) {
-        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(&vt_lds[(32 * d + l32) * kVStride + 16 * kk + 8 * g]);
-        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kk], o[d], 0, 0, 0);
-      }
-    }
-    }
-    if (more) store_tile((j + 1) & 1);  // the other buffer: last read before the previous barrier
+    // tile j + 1 goes to the buffer that tile j - 2 used: last read before
+    // the previous barrier
+    if (more) store_tile(nxt);
     __syncthreads();
+    cur = nxt;
+  }
+  if (pend) {
+    rescale_prev();
+    pv_step(vt_lds2[cur == 0 ? 2 : cur - 1]);
   }
 
   // O^T[dim][row]: lane holds row l32, dims 32 d + 8 (i / 4) + 4 g + i % 4

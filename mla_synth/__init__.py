@@ -45,6 +45,9 @@ CONFIGS = {
                          shuffle=True, causal=False, topk=0, seed=3),
     "fp8_head_slice": dict(B=128, Sq=2, H=16, lens=("fixed", 4096), kv="fp8",
                            shuffle=True, causal=True, topk=0, seed=4),
+    # dsv3_decode with every sequence at the 8K maximum (a supplementary size)
+    "dsv3_decode_max": dict(B=64, Sq=1, H=128, lens=("fixed", 8192), kv="bf16",
+                            shuffle=True, causal=False, topk=0, seed=6),
     "dsa_sparse": dict(B=32, Sq=1, H=128, lens=("fixed", 65536), kv="bf16",
                        shuffle=True, causal=False, topk=1024, seed=5,
                        sel_blocks=16, init_blocks=1, local_blocks=2),
@@ -215,6 +218,7 @@ def shrink(name: str, **over) -> dict:
         "long_context": dict(B=2, lens=("fixed", 1500)),
         "fp8_head_slice": dict(B=4, lens=("fixed", 333)),
         "dsa_sparse": dict(B=2, lens=("fixed", 2048), topk=512, sel_blocks=8),
+        "dsv3_decode_max": dict(B=2, lens=("fixed", 640)),
     }[name]
     small.update(over)
     return config(name, **small)

@@ -52,16 +52,27 @@ __global__ __launch_bounds__(256) void head_gemm_kernel(ProjArgs a) {
   const bf16x8* wrow = reinterpret_cast<const bf16x8*>(a.w + ((size_t)h * N + n0 + l32) * K + k_off + 8 * g);
 #pragma unroll
   for (int ks = 0; ks < KS; ks++) wf[ks] = wrow[2 * ks];
-  for (int mt = 0; mt < kRowsPerBlock / 32; mt++) {
+  // every row tile's activations are requested together with the weights:
+  // one memory round trip for the whole workgroup
+  constexpr int kMT = kRowsPerBlock / 32;
+  bf16x8 av_all[kMT][KS];
+#pragma unroll
+  for (int mt = 0; mt < kMT; mt++) {
+    const int m0 = m_base + 32 * mt;
+    const int row = m0 + l32;
+    const bool ok = m0 < M && row < M;
+    const bf16x8* arow =
+        reinterpret_cast<const bf16x8*>(a.a + ((size_t)(ok ? row : 0) * H + h) * K + k_off + 8 * g);
+#pragma unroll
+    for (int ks = 0; ks < KS; ks++) av_all[mt][ks] = ok ? arow[2 * ks] : bf16x8{};
+  }
+#pragma unroll
+  for (int mt = 0; mt < kMT; mt++) {
     const int m0 = m_base + 32 * mt;
     if (m0 >= M) break;  // uniform over the workgroup
     const int row = m0 + l32;
     const bool ok = row < M;
-    const bf16x8* arow =
-        reinterpret_cast<const bf16x8*>(a.a + ((size_t)(ok ? row : m0) * H + h) * K + k_off + 8 * g);
-    bf16x8 av[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ks++) av[ks] = ok ? arow[2 * ks] : bf16x8{};
+    const bf16x8* av = av_all[mt];
     f32x16 acc = {};
 #pragma unroll
     for (int ks = 0; ks < KS; ks++) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[ks], av[ks], acc, 0, 0, 0);

@@ -137,3 +137,12 @@ def test_append_then_decode_matches_oracle(kv):
         ref["kv_scales"] = torch.from_numpy(sc2)
     ref_out, ref_lse = oracle.decode(ref)
     check(out, lse, ref_out, ref_lse, what=f"append+decode {kv}")
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_append_rows_straddling_a_page_boundary(kv):
+    """Four new tokens per sequence that end past a 64-token page edge (62..65, 126..129, 61..64)."""
+    inp = S.make_inputs(S.shrink("dsv3_decode", B=3, kv=kv, lens=("fixed", 200)), poison=False)
+    L = torch.tensor([66, 128 + 2, 64 + 1], dtype=torch.int32)
+    new = _new_rows(3, 4, 25)
+    _assert_same(*_append_both(inp, new, L=L))

@@ -241,7 +241,7 @@ def sampled_check(inp, nrows=40, seed=0, **kw):
     assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
 
 
-@pytest.mark.parametrize("name", ["dsv3_decode", "long_context", "fp8_head_slice", "dsa_sparse"])
+@pytest.mark.parametrize("name", ["dsv3_decode", "dsv3_decode_max", "long_context", "fp8_head_slice", "dsa_sparse"])
 def test_named_workload_full_size_sampled(name):
     inp = S.make_inputs(S.config(name), unselected="nan", poison=True)
     sampled_check(inp)

@@ -312,7 +312,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the path is single-GPU; sharding is described in DESIGN.md)", file=sys.stderr)
+              "(each GPU would run this path on its own share of the batch)", file=sys.stderr)
         sys.exit(2)
 
     if args.op == "append":

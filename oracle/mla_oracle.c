@@ -31,8 +31,9 @@
  *     sparse: the listed positions indices[b][s][t] with 0 <= idx < L
  *             (DSA reads only the k selected tokens, same page, §1.2 and §4.2).
  *   Paging: token j of sequence b lives in page block_table[b][j / 64] at row
- *   j % 64.  A token whose page entry lies outside [0, num_pages) is not
- *   visible (the kernels treat it the same way).
+ *   j % 64.  A token whose logical page j / 64 is at or past the table's row
+ *   length (bt_stride), or whose page entry lies outside [0, num_pages), is
+ *   not visible: the table gives it no resident page.
  *
  *   fp8 cache: each element is an OCP e4m3fn code (1 sign, 4 exponent bits
  *   with bias 7, 3 mantissa bits, subnormals, S.1111.111 = NaN, no infinity)
@@ -108,8 +109,11 @@ static double kv_elem(const job_t *J, long p, int r, int d) {
   return bf16_bits_to_double(((const uint16_t *)J->kv)[off]);
 }
 
-/* Physical (page, row) of logical token j of sequence b; 0 if not resident. */
+/* Physical (page, row) of logical token j of sequence b; 0 if not resident.
+ * The block table row of sequence b holds bt_stride entries: a token whose
+ * logical page j / 64 is at or past that has no entry and is not visible. */
 static int locate(const job_t *J, int b, long j, long *p, int *r) {
+  if (j < 0 || j / OR_PAGE >= J->bt_stride) return 0;
   long pg = J->block_table[(long)b * J->bt_stride + j / OR_PAGE];
   if (pg < 0 || pg >= J->num_pages) return 0;
   *p = pg;

@@ -33,8 +33,8 @@ def _f64(t):
 def latent_rows(inp: dict, b: int, positions) -> np.ndarray:
     """[n, 576] float64 latent rows of sequence b at logical `positions`.
 
-    Positions whose page entry is outside the pool give NaN rows (callers
-    drop them before use)."""
+    Every position must have a block-table entry (logical page below the
+    table's row length); `visible_positions` only returns such positions."""
     kv = inp["kv_pages"]
     bt = inp["block_table"].numpy()
     pos = np.asarray(positions, dtype=np.int64)
@@ -56,6 +56,9 @@ def visible_positions(inp: dict, b: int, s: int) -> np.ndarray:
     else:
         last = L - inp["Sq"] + s if inp["causal"] else L - 1
         pos = np.arange(0, min(last, L - 1) + 1, dtype=np.int64)
+    # a logical page at or past the table's row length has no entry, and a
+    # page entry outside the pool names no page: either way not resident
+    pos = pos[pos // PAGE < bt.shape[1]]
     if pos.size:
         pg = bt[b, pos // PAGE]
         pos = pos[(pg >= 0) & (pg < P)]

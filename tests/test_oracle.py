@@ -237,6 +237,71 @@ def test_empty_sequence_gives_zero_and_minus_inf():
     assert np.all(np.isfinite(lse[1]))
 
 
+
+# ---------------------------------------------------------------- the table's row length
+def _narrow_table(inp, stride):
+    """The same cache with each block-table row cut to `stride` entries."""
+    return dict(inp, block_table=inp["block_table"][:, :stride].contiguous())
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_tokens_past_the_table_row_are_invisible_dense(kv):
+    # Sequence 0 is longer than its 3-entry table row covers (192 tokens);
+    # sequence 1's row follows it in memory and holds valid pages, so an
+    # oracle that read past the row would pick up foreign tokens here.
+    inp = _custom(B=3, lens=(300, 250, 260), H=4, kv=kv, seed=21)
+    cut = _narrow_table(inp, 3)
+    got = oracle.decode(cut)
+    # the same as if every sequence were only as long as its table row
+    short = dict(cut, cache_seqlens=torch.clamp(inp["cache_seqlens"], max=3 * 64))
+    want = oracle.decode(short)
+    assert np.array_equal(got[0], want[0]) and np.array_equal(got[1], want[1])
+    # and not the same as the untruncated cache (the cut matters)
+    full = oracle.decode(inp)
+    assert not np.allclose(full[0], got[0])
+    # the NumPy oracle reads the table the same way
+    ref = R.decode(cut)
+    np.testing.assert_allclose(got[0], ref[0], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(got[1], ref[1], rtol=1e-12, atol=1e-12)
+
+
+def test_tokens_past_the_table_row_are_invisible_causal():
+    # Sq = 2, causal: both queries' visible sets are cut at the row's end
+    cfg = dict(B=2, Sq=2, H=4, lens=("list", (200, 150)), kv="bf16", shuffle=True,
+               causal=True, topk=0, name="custom")
+    inp = S.make_inputs(cfg, seed=22)
+    cut = _narrow_table(inp, 2)
+    got = oracle.decode(cut)
+    ref = R.decode(cut)
+    np.testing.assert_allclose(got[0], ref[0], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(got[1], ref[1], rtol=1e-12, atol=1e-12)
+    # query 1 of each sequence now sees exactly tokens 0..127
+    one = dict(cut, Sq=1, causal=False, q_nope=inp["q_nope"][:, 1:].contiguous(),
+               q_rope=inp["q_rope"][:, 1:].contiguous(),
+               cache_seqlens=torch.full((2,), 128, dtype=torch.int32))
+    o1, l1 = oracle.decode(one)
+    assert np.array_equal(got[0][:, 1], o1[:, 0]) and np.array_equal(got[1][:, 1], l1[:, 0])
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_tokens_past_the_table_row_are_invisible_sparse(kv):
+    inp = _custom(B=2, lens=(400, 300), H=4, kv=kv, seed=23)
+    cut = _narrow_table(inp, 4)   # 256 tokens per sequence have a page
+    topk = 96
+    g_ = torch.Generator().manual_seed(24)
+    ix = torch.full((2, 1, topk), -1, dtype=torch.int32)
+    for b, L in enumerate((400, 300)):
+        ix[b, 0] = torch.randperm(L, generator=g_)[:topk].to(torch.int32)
+    assert (ix >= 256).any() and (ix < 256).any()
+    got = oracle.decode(cut, indices=ix)
+    # entries past the row behave exactly like the -1 padding
+    want = oracle.decode(cut, indices=torch.where(ix >= 256, torch.full_like(ix, -1), ix))
+    assert np.array_equal(got[0], want[0]) and np.array_equal(got[1], want[1])
+    ref = R.decode(dict(cut, indices=ix))
+    np.testing.assert_allclose(got[0], ref[0], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(got[1], ref[1], rtol=1e-12, atol=1e-12)
+
+
 # ---------------------------------------------------------------- sparse
 def test_sparse_equals_dense_with_complement_masked():
     cfg = S.shrink("dsa_sparse")

@@ -27,10 +27,12 @@ namespace {
 
 constexpr int kSelThreads = 256;
 
-// Larger score -> larger key; NaN counts as -inf.
+// Larger score -> larger key; NaN counts as -inf.  -0.0 and +0.0 are the
+// same score, so they get the same key (a tie, resolved by block order).
 __device__ __forceinline__ unsigned score_key(float x) {
   if (x != x) x = -__builtin_inff();
-  const unsigned u = __float_as_uint(x);
+  unsigned u = __float_as_uint(x);
+  if (u == 0x80000000u) u = 0u;
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 

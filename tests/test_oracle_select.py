@@ -40,6 +40,19 @@ def test_ties_take_the_lower_block_and_nan_is_lowest():
     assert D.select_blocks(sc2, 10, 6, 1, 2) == [0, 1, 2, 3, 8, 9]
 
 
+def test_signed_zeros_are_one_score():
+    # -0.0 and +0.0 are the same real number: at the selection threshold
+    # they tie, and the tie goes to the lower block whatever the signs.
+    base = np.full(10, -1.0, dtype=np.float32)
+    for z3, z5 in ((-0.0, 0.0), (0.0, -0.0), (0.0, 0.0), (-0.0, -0.0)):
+        sc = base.copy()
+        sc[3], sc[5] = z3, z5
+        assert D.select_blocks(sc, 10, 4, 1, 2) == [0, 3, 8, 9], (z3, z5)
+    # two of them taken, the rest of the middle lower: both zeros selected
+    sc = base.copy()
+    sc[3], sc[5] = -0.0, 0.0
+    assert D.select_blocks(sc, 10, 5, 1, 2) == [0, 3, 5, 8, 9]
+
 def test_order_preserving_changes_keep_the_selection():
     rng = np.random.default_rng(9)
     sc = rng.standard_normal((2, 1, 200)).astype(np.float32)

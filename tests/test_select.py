@@ -53,6 +53,29 @@ def test_ties_nan_and_ragged_causal_lengths():
     _eq(*_both(sc, L, Sq))
 
 
+
+def test_signed_zeros_tie_at_the_threshold():
+    # block 3 holds -0.0 and block 5 +0.0, the rest of the middle -1: the two
+    # zeros are one score, so the tie goes to the lower block
+    base = np.full(10, -1.0, dtype=np.float32)
+    rows = []
+    for z3, z5 in ((-0.0, 0.0), (0.0, -0.0), (0.0, 0.0), (-0.0, -0.0)):
+        r = base.copy()
+        r[3], r[5] = z3, z5
+        rows.append(r)
+    sc = np.stack(rows)[:, None, :]
+    L = np.full(4, 10 * 64, dtype=np.int32)
+    got, want = _both(sc, L, 1, n_select=4, n_init=1, n_local=2)
+    _eq(got, want)
+    for b in range(4):
+        assert sorted(set((got[b, 0][got[b, 0] >= 0] // 64).tolist())) == [0, 3, 8, 9]
+    # mixed signed zeros among heavy ties over a wider row
+    rng = np.random.default_rng(8)
+    sc = rng.integers(-1, 2, (6, 2, 200)).astype(np.float32)
+    sc[sc == 0] = np.where(rng.random(int((sc == 0).sum())) < 0.5, -0.0, 0.0)
+    L = rng.integers(1, 200 * 64 + 1, 6).astype(np.int32)
+    _eq(*_both(sc, L, 2))
+
 @pytest.mark.parametrize("n_select,n_init,n_local", [(16, 0, 0), (16, 8, 8), (1, 0, 1), (40, 3, 5),
                                                      (256, 1, 2)])
 def test_selection_shapes(n_select, n_init, n_local):

@@ -57,6 +57,20 @@ def lib():
     return _lib
 
 
+def default_threads() -> int:
+    """Worker threads for the oracle: OMP_NUM_THREADS when set (the CPU share
+    a job is given), else every core this process may run on."""
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        n = int(env)
+    else:
+        try:
+            n = len(os.sched_getaffinity(0))
+        except AttributeError:
+            n = os.cpu_count() or 1
+    return max(1, min(n, 256))
+
+
 def _np(t, dtype):
     """Contiguous numpy view of a CPU tensor / array with the given raw dtype."""
     import torch
@@ -110,7 +124,7 @@ def decode(inp: dict, rows=None, nthreads: int | None = None, indices=None, caus
     out = np.zeros((n, 512), dtype=np.float64)
     lse = np.zeros((n,), dtype=np.float64)
     if nthreads is None:
-        nthreads = os.cpu_count() or 1
+        nthreads = default_threads()
     ptr = lambda a: None if a is None else a.ctypes.data
     rc = lib().oracle_mla_decode(
         ptr(qn), ptr(qr), ptr(kv), ptr(sc), int(fp8), int(kv.shape[0]), ptr(bt), int(bt.shape[1]),

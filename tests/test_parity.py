@@ -1,12 +1,13 @@
 """GPU parity: the HIP path (through the C ABI) against the CPU oracle.
 
-Tolerances: bf16 out max-abs <= 1e-2 and relative L2 <= 5e-3 over the
-compared rows; lse max-abs <= 1e-3.  The named workloads are held to exactly
-these.  The edge-case tests use very short sequences whose outputs are
-single cached values or averages of two or three (|out| up to ~4), where
-rounding the exact result to bf16 alone can exceed 1e-2; there each element
-may also be off by one bf16 rounding of the reference, 2^-8 |ref|.  Rows the
-oracle says see no token must come back as out = 0, lse = -inf exactly.
+Tolerances: bf16 out max-abs <= 1e-2 and relative L2 <= 5e-3 over the whole
+out tensor; lse max-abs <= 1e-3.  One exception, per row: a row that sees at
+most three tokens has an output that is a single cached value or an average
+of two or three (|out| up to ~4), where rounding the exact result to bf16
+alone can exceed 1e-2; each element of such a row may also be off by one
+bf16 rounding of the reference, 2^-8 |ref|.  Rows the oracle says see no
+token must come back as out = 0, lse = -inf exactly.  The named workloads
+are compared in full at their full sizes, every row against the oracle.
 """
 import os
 import sys
@@ -44,7 +45,17 @@ def run(g, num_wg=0, planned=False, workspace=None):
                     num_wg=num_wg, planned=planned, workspace=workspace)
 
 
-def check(out, lse, ref_out, ref_lse, what="", edge=False):
+def visible_counts(inp):
+    """Tokens each query row sees, [B*Sq*H] (the oracle's visibility rule)."""
+    from oracle import ref_numpy as R
+    B, Sq, H = inp["B"], inp["Sq"], inp["H"]
+    n = np.array([[R.visible_positions(inp, b, s).size for s in range(Sq)] for b in range(B)])
+    return np.repeat(n.reshape(-1), H)
+
+
+def check(out, lse, ref_out, ref_lse, what="", nvis=None):
+    """Compare with the oracle; nvis (tokens seen per row) widens the bound
+    of rows that see at most three tokens (see the module docstring)."""
     got = out.float().cpu().double().numpy().reshape(-1, 512)
     gl = lse.cpu().double().numpy().reshape(-1)
     ro = ref_out.reshape(-1, 512)
@@ -54,23 +65,27 @@ def check(out, lse, ref_out, ref_lse, what="", edge=False):
     assert np.all(got[empty] == 0), f"{what}: empty rows must give out=0"
     assert np.all(np.isfinite(got)), f"{what}: non-finite output"
     assert np.all(np.isfinite(gl[~empty])), f"{what}: non-finite lse"
-    bound = OUT_ABS + (2.0 ** -8) * np.abs(ro) if edge else OUT_ABS
+    bound = np.full(ro.shape, OUT_ABS)
+    if nvis is not None:
+        few = np.asarray(nvis).reshape(-1) <= 3
+        bound[few] += (2.0 ** -8) * np.abs(ro[few])
     excess = (np.abs(got - ro) - bound).max() if got.size else -1.0
     err = np.abs(got - ro).max() if got.size else 0.0
     nrm = np.linalg.norm(ro)
     rel = np.linalg.norm(got - ro) / nrm if nrm > 0 else 0.0
     lerr = np.abs(gl[~empty] - rl[~empty]).max() if (~empty).any() else 0.0
-    print(f"{what}: max-abs {err:.2e} rel-L2 {rel:.2e} lse {lerr:.2e}", flush=True)
+    print(f"{what}: rows {ro.shape[0]} max-abs {err:.2e} rel-L2 {rel:.2e} lse {lerr:.2e}", flush=True)
     assert excess <= 0, f"{what}: out max-abs {err} (beyond the bound by {excess})"
     assert rel <= OUT_REL, f"{what}: out rel-L2 {rel}"
     assert lerr <= LSE_ABS, f"{what}: lse max-abs {lerr}"
 
 
-def full_check(inp, edge=True, **kw):
+def full_check(inp, **kw):
+    print(f"{inp.get('name', '')} {kw}", flush=True)
     out, lse = run(dev(inp), **kw)
     torch.cuda.synchronize()
     ref = oracle.decode(inp)
-    check(out, lse, ref[0], ref[1], inp.get("name", "") + f" {kw}", edge=edge)
+    check(out, lse, ref[0], ref[1], inp.get("name", "") + f" {kw}", nvis=visible_counts(inp))
     return out, lse
 
 
@@ -84,11 +99,7 @@ def custom(B=1, Sq=1, H=16, lens=(256,), kv="bf16", causal=False, topk=0, seed=7
 # ---------------------------------------------------------------- named workloads, small
 @pytest.mark.parametrize("name", list(S.CONFIGS))
 def test_named_workload_shrunk(name):
-    full_check(S.make_inputs(S.shrink(name), unselected="nan"), edge=False)
-
-
-def test_tiny_workload_full_size():
-    full_check(S.make_inputs(S.config("tiny")), edge=False)
+    full_check(S.make_inputs(S.shrink(name), unselected="nan"))
 
 
 # ---------------------------------------------------------------- shapes
@@ -148,7 +159,7 @@ def test_plan_once_then_planned_calls():
     torch.cuda.synchronize()
     assert torch.equal(out1, out2) and torch.equal(out1, out3) and torch.equal(lse1, lse3)
     ref = oracle.decode(inp)
-    check(out1, lse1, ref[0], ref[1], "planned")
+    check(out1, lse1, ref[0], ref[1], "planned", nvis=visible_counts(inp))
 
 
 @pytest.mark.parametrize("name", ["dsv3_decode", "fp8_head_slice", "dsa_sparse"])
@@ -187,7 +198,7 @@ def test_graph_replay_matches_eager(name):
         assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse), f"replay {rep} differs"
         assert torch.equal(other[0], ref_out)
     ref = oracle.decode(inp)
-    check(out, lse, ref[0], ref[1], name + " graph replay")
+    check(out, lse, ref[0], ref[1], name + " graph replay", nvis=visible_counts(inp))
 
 
 def test_out_of_range_block_table_entries_are_skipped():
@@ -225,23 +236,43 @@ def test_sparse_all_invalid_gives_empty():
     full_check(inp)
 
 
-# ---------------------------------------------------------------- full-size workloads, sampled rows
-def sampled_check(inp, nrows=40, seed=0, **kw):
-    out, lse = run(dev(inp), **kw)
-    torch.cuda.synchronize()
-    R = inp["B"] * inp["Sq"] * inp["H"]
-    rng = np.random.default_rng(seed)
-    rows = sorted(set([0, R - 1] + rng.choice(R, size=min(nrows, R), replace=False).tolist()))
-    ref_o, ref_l = oracle.decode(inp, rows=rows)
-    o = out.reshape(-1, 512)[rows]
-    l = lse.reshape(-1)[rows]
-    check(o, l, ref_o, ref_l, inp["name"] + " sampled")
-    # every row, not only the sampled ones, must be finite: poisoned (NaN)
-    # cache rows past each sequence end would surface here if read
-    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+# ---------------------------------------------------------------- a table row shorter than the sequence
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_tokens_past_the_table_row_are_invisible_dense(kv):
+    # every sequence is longer than its 3-entry table row (192 tokens) covers;
+    # the rows that follow in memory hold valid pages of other sequences
+    inp = custom(B=3, Sq=2, H=64, lens=(300, 250, 200), kv=kv, causal=True, seed=31)
+    inp["block_table"] = inp["block_table"][:, :3].contiguous()
+    assert (inp["cache_seqlens"] > 64 * 3).all()
+    full_check(inp)
 
 
-@pytest.mark.parametrize("name", ["dsv3_decode", "dsv3_decode_max", "long_context", "fp8_head_slice", "dsa_sparse"])
-def test_named_workload_full_size_sampled(name):
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_tokens_past_the_table_row_are_invisible_sparse(kv):
+    inp = custom(B=2, Sq=1, H=128, lens=(400, 300), kv=kv, seed=32)
+    inp["block_table"] = inp["block_table"][:, :4].contiguous()   # 256 tokens have a page
+    topk = 130
+    g_ = torch.Generator().manual_seed(33)
+    ix = torch.full((2, 1, topk), -1, dtype=torch.int32)
+    for b, L in enumerate((400, 300)):
+        ix[b, 0] = torch.randperm(L, generator=g_)[:topk].to(torch.int32)
+    assert (ix >= 256).any()
+    inp["indices"] = ix
+    inp["topk"] = topk
+    full_check(inp)
+
+
+# ---------------------------------------------------------------- full-size workloads, every row
+@pytest.mark.parametrize("name", ["tiny", "dsv3_decode", "dsv3_decode_max", "long_context",
+                                  "fp8_head_slice", "dsa_sparse"])
+def test_named_workload_full_size(name):
+    """The whole out/lse tensors at the sizes the benchmark times, in its
+    launch configuration, against the oracle on every row; cache rows past
+    each sequence end (and unselected pages) hold NaN."""
     inp = S.make_inputs(S.config(name), unselected="nan", poison=True)
-    sampled_check(inp)
+    print(f"{name}: B={inp['B']} Sq={inp['Sq']} H={inp['H']} oracle threads "
+          f"{oracle.default_threads()}", flush=True)
+    out, lse = run(dev(inp))
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.decode(inp)
+    check(out, lse, ref_o, ref_l, name + " full size")

@@ -39,22 +39,22 @@ def test_prefill_matches_oracle(B, T, H, causal):
     assert err <= 1e-2 and rel <= 5e-3 and lerr <= 1e-3, (err, rel, lerr)
 
 
-def test_prefill_sampled_rows_at_bench_size():
+def test_prefill_whole_heads_at_bench_size():
+    """Every row of three heads at the size the benchmark times (B=1, T=4096,
+    H=128, causal), against the oracle run on those heads alone (heads do
+    not interact)."""
     B, T, H = 1, 4096, 128
     q, k, v = _rand((B, T, H, 192), 11), _rand((B, T, H, 192), 12), _rand((B, T, H, 128), 13)
     scale = 1 / np.sqrt(192)
     print(f"prefill B={B} T={T} H={H}", flush=True)
     out, lse = mla().prefill(q.cuda(), k.cuda(), v.cuda(), scale)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(0)
     heads = [0, 77, 127]
-    ts = [0, 1, 127, 128, 2047, 4095] + list(rng.integers(0, T, 4))
-    qs, ks, vs = q.double().numpy(), k.double().numpy(), v.double().numpy()
-    for h in heads:
-        for t in ts:
-            # causal row t = the oracle's attention of that one query over tokens 0..t
-            ro, rl = PF.prefill(qs[:, t:t + 1, h:h + 1], ks[:, : t + 1, h:h + 1], vs[:, : t + 1, h:h + 1],
-                                scale, causal=False)
-            got = out[0, t, h].float().cpu().double().numpy()
-            assert np.abs(got - ro[0, 0, 0]).max() <= 1e-2
-            assert abs(float(lse[0, t, h]) - rl[0, 0, 0]) <= 1e-3
+    qs, ks, vs = (x[:, :, heads].double().numpy() for x in (q, k, v))
+    ro, rl = PF.prefill(qs, ks, vs, scale, causal=True)
+    got = out[:, :, heads].float().cpu().double().numpy()
+    err = np.abs(got - ro).max()
+    rel = np.linalg.norm(got - ro) / np.linalg.norm(ro)
+    lerr = np.abs(lse[:, :, heads].cpu().double().numpy() - rl).max()
+    print(f"prefill heads {heads}: max-abs {err:.2e} rel-L2 {rel:.2e} lse {lerr:.2e}", flush=True)
+    assert err <= 1e-2 and rel <= 5e-3 and lerr <= 1e-3, (err, rel, lerr)

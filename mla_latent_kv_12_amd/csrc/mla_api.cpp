@@ -40,7 +40,6 @@ int device_cus() {
 }
 
 constexpr int kMaxWg = 1 << 16;
-constexpr int kStagePlan = 1, kStageAttend = 2, kStageCombine = 4;
 
 // Folds the request into scheduling units; returns false on invalid sizes.
 bool make_geometry(int B, int Sq, int H, int topk, int num_wg, mla::Geometry* g) {
@@ -60,6 +59,7 @@ bool make_geometry(int B, int Sq, int H, int topk, int num_wg, mla::Geometry* g)
   if (units > (1 << 24)) return false;
   g->n_units = (int)units;
   g->m_unit = (int)(m_full < mla::kMaxUnitRows ? m_full : mla::kMaxUnitRows);
+  g->split_rows = g->m_unit > 64 ? 128 : g->m_unit > 32 ? 64 : 32;
   g->num_wg = num_wg;
   g->max_splits = num_wg + g->n_units;
   return true;
@@ -96,14 +96,20 @@ mla_status fill_sched_args(const mla::Geometry& g, const int32_t* seqlens, void*
   a->row_blocks = g.row_blocks;
   a->n_units = g.n_units;
   a->num_wg = g.num_wg;
+  a->split_rows = g.split_rows;
   return MLA_OK;
 }
 
-mla_status run(const void* q_nope, const void* q_rope, const void* kv_pages, const float* kv_scales,
-               mla_kv_dtype kv_dtype, int num_pages, const int32_t* block_table, int bt_stride,
-               const int32_t* cache_seqlens, const int32_t* indices, int topk, int B, int Sq,
-               int H, float softmax_scale, int causal, void* out, float* lse, void* workspace,
-               size_t ws_bytes, int num_wg, int planned, hipStream_t stream, int stages = 7) {
+}  // namespace
+
+// Validates a decode request and enqueues its stages (plan unless planned,
+// main pass, combine) on `stream` with the given workspace.
+mla_status mla::run_decode(const void* q_nope, const void* q_rope, const void* kv_pages,
+                           const float* kv_scales, mla_kv_dtype kv_dtype, int num_pages,
+                           const int32_t* block_table, int bt_stride, const int32_t* cache_seqlens,
+                           const int32_t* indices, int topk, int B, int Sq, int H,
+                           float softmax_scale, int causal, void* out, float* lse, void* workspace,
+                           size_t ws_bytes, int num_wg, int planned, hipStream_t stream, int stages) {
   g_err[0] = 0;
   if (!q_nope || !q_rope || !kv_pages || !block_table || !cache_seqlens || !out || !lse)
     return fail(MLA_ERR_NULL, "a required tensor pointer is NULL");
@@ -151,22 +157,22 @@ mla_status run(const void* q_nope, const void* q_rope, const void* kv_pages, con
   a.scale_log2 = softmax_scale * 1.44269504088896340736f;
 
   hipError_t e;
-  if ((stages & kStagePlan) && !planned) {
+  if ((stages & mla::kStagePlan) && !planned) {
     e = mla::launch_plan(g, a, stream);
     if (e != hipSuccess) return fail(MLA_ERR_HIP, "plan launch: %s", hipGetErrorString(e));
   }
-  if (stages & kStageAttend) {
+  if (stages & mla::kStageAttend) {
     e = mla::launch_decode(g, a, kv_dtype == MLA_KV_FP8_E4M3, stream);
     if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
   }
-  if (stages & kStageCombine) {
+  if (stages & mla::kStageCombine) {
     e = mla::launch_combine(g, a, stream);
     if (e != hipSuccess) return fail(MLA_ERR_HIP, "combine launch: %s", hipGetErrorString(e));
   }
   return MLA_OK;
 }
 
-}  // namespace
+mla_status mla::fail_status(mla_status s, const char* msg) { return fail(s, "%s", msg); }
 
 extern "C" {
 
@@ -207,7 +213,7 @@ mla_status mla_decode(const void* q_nope, const void* q_rope, const void* kv_pag
                       int B, int Sq, int H, float softmax_scale, int causal, void* out,
                       float* lse, void* workspace, size_t ws_bytes, int num_wg, int planned,
                       hipStream_t stream) {
-  return run(q_nope, q_rope, kv_pages, kv_scales, kv_dtype, num_pages, block_table, bt_stride,
+  return mla::run_decode(q_nope, q_rope, kv_pages, kv_scales, kv_dtype, num_pages, block_table, bt_stride,
              cache_seqlens, nullptr, 0, B, Sq, H, softmax_scale, causal, out, lse, workspace,
              ws_bytes, num_wg, planned, stream);
 }
@@ -221,7 +227,7 @@ mla_status mla_sparse_decode(const void* q_nope, const void* q_rope, const void*
                              hipStream_t stream) {
   g_err[0] = 0;
   if (topk <= 0) return fail(MLA_ERR_SHAPE, "topk must be >= 1 (got %d)", topk);
-  return run(q_nope, q_rope, kv_pages, kv_scales, kv_dtype, num_pages, block_table, bt_stride,
+  return mla::run_decode(q_nope, q_rope, kv_pages, kv_scales, kv_dtype, num_pages, block_table, bt_stride,
              cache_seqlens, indices, topk, B, Sq, H, softmax_scale, 0, out, lse, workspace, ws_bytes,
              num_wg, planned, stream);
 }
@@ -235,9 +241,9 @@ mla_status mla_attend(const void* q_nope, const void* q_rope, const void* kv_pag
   g_err[0] = 0;
   if (topk < 0 || (topk > 0) != (indices != nullptr))
     return fail(MLA_ERR_SHAPE, "indices and topk must be both set (sparse) or NULL and 0 (dense)");
-  return run(q_nope, q_rope, kv_pages, kv_scales, kv_dtype, num_pages, block_table, bt_stride,
+  return mla::run_decode(q_nope, q_rope, kv_pages, kv_scales, kv_dtype, num_pages, block_table, bt_stride,
              cache_seqlens, indices, topk, B, Sq, H, softmax_scale, causal, out, lse, workspace,
-             ws_bytes, num_wg, 1, stream, kStageAttend);
+             ws_bytes, num_wg, 1, stream, mla::kStageAttend);
 }
 
 mla_status mla_combine(const int32_t* cache_seqlens, int B, int Sq, int H, int topk, void* out,

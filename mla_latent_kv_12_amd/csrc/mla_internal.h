@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "mla.h"
+
 namespace mla {
 
 constexpr int kDC = 512;             // latent dims (value part)
@@ -37,6 +39,7 @@ struct Geometry {
   int row_blocks;  // ceil(m_full / 128)
   int n_units;     // n_su * row_blocks
   int m_unit;      // min(m_full, 128): selects the kernel shape
+  int split_rows;  // rows of one split partial: 32 * waves of the kernel shape (32, 64, 128)
   int num_wg;      // persistent workgroups
   int max_splits;  // num_wg + n_units
 };
@@ -45,8 +48,8 @@ struct WsLayout {
   size_t work;   // int32 [(num_wg + 1) * 2]   (first unit, first tile) per WG
   size_t cost;   // int32 [n_units + 1]        prefix of per-unit cost
   size_t meta;   // int32 [n_units * 4]        n_tiles, split_base, n_splits, g_first
-  size_t plse;   // f32   [max_splits * 128]   partial log2-sum-exp
-  size_t po;     // f32   [max_splits * 128 * 512] partial normalised outputs
+  size_t plse;   // f32   [max_splits * split_rows]   partial log2-sum-exp
+  size_t po;     // f32   [max_splits * split_rows * 512] partial normalised outputs
   size_t zero;   // 1280 zero bytes: copy source for cache rows that are not visible
   size_t total;
 };
@@ -72,7 +75,7 @@ struct DecodeArgs {
   int bt_stride;
   int num_pages;
   int B, Sq, H, topk;
-  int n_su, m_full, row_blocks, n_units, num_wg;
+  int n_su, m_full, row_blocks, n_units, num_wg, split_rows;
   int causal;
   float scale_log2;  // softmax_scale * log2(e)
 };
@@ -120,6 +123,21 @@ struct PrefillArgs {
   float scale;
 };
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
+// Stages of a decode call (bit mask).
+constexpr int kStagePlan = 1, kStageAttend = 2, kStageCombine = 4, kStagesAll = 7;
+
+// The decode behind mla_decode / mla_sparse_decode / mla_attend: validates
+// everything on the host, then enqueues the selected stages with the given
+// workspace.  Sets the calling thread's error string on failure.
+mla_status run_decode(const void* q_nope, const void* q_rope, const void* kv_pages,
+                      const float* kv_scales, mla_kv_dtype kv_dtype, int num_pages,
+                      const int32_t* block_table, int bt_stride, const int32_t* cache_seqlens,
+                      const int32_t* indices, int topk, int B, int Sq, int H, float softmax_scale,
+                      int causal, void* out, float* lse, void* workspace, size_t ws_bytes,
+                      int num_wg, int planned, hipStream_t stream, int stages = kStagesAll);
+// Records `msg` as the calling thread's error detail and returns s.
+mla_status fail_status(mla_status s, const char* msg);
 
 hipError_t launch_plan(const Geometry& g, const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode(const Geometry& g, const DecodeArgs& a, bool fp8, hipStream_t stream);

@@ -1019,7 +1019,7 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
       } else {
         // Partials are stored in fragment order (see combine_kernel): each
         // store writes 1 KB of consecutive bytes, one 16-byte piece per lane.
-        float* dst = a.ws_po + (size_t)split * (kMaxUnitRows * kDC) + 4 * ln;
+        float* dst = a.ws_po + (size_t)split * (32 * R * kDC) + 4 * ln;
 #pragma unroll
         for (int dbl = 0; dbl < DB; dbl++) {
           const int db = DB * rg + dbl;
@@ -1031,7 +1031,7 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
             *reinterpret_cast<f32x4*>(dst + 256 * ((rb * 16 + db) * 4 + q)) = w;
           }
         }
-        if (lse_writer) a.ws_plse[(size_t)split * kMaxUnitRows + r] = lse2;
+        if (lse_writer) a.ws_plse[(size_t)split * (32 * R) + r] = lse2;
       }
     }
   };
@@ -1208,7 +1208,8 @@ MLA_WIDE_KERNEL(decode_fp8_sparse_r2, true, true, 2)
 // Combine: for units with >= 2 splits merge the partial (O/l, log2 lse)
 // results; units with no tokens at all get out = 0, lse = -inf.
 //
-// Partial layout per split: 256 blocks of 1 KB in fragment order.  Block
+// Partial layout per split (32 * R rows, R the waves of the kernel shape):
+// 64 * R blocks of 1 KB in fragment order.  Block
 // (rb, db, q) = (rb * 16 + db) * 4 + q holds, at lane L = 32 g + l (16 bytes
 // each), row 32 rb + l, dims 32 db + 8 q + 4 g .. +3: the order in which a
 // wave's accumulators leave the registers.  Each 64-thread group of a block
@@ -1251,16 +1252,16 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; j++) {
       const size_t sp = (size_t)(base + i + j);
-      l4[j] = a.ws_plse[sp * kMaxUnitRows + r];
-      v4[j] = *reinterpret_cast<const f32x4*>(a.ws_po + sp * (kMaxUnitRows * kDC) + frag);
+      l4[j] = a.ws_plse[sp * a.split_rows + r];
+      v4[j] = *reinterpret_cast<const f32x4*>(a.ws_po + sp * ((size_t)a.split_rows * kDC) + frag);
     }
 #pragma unroll
     for (int j = 0; j < 4; j++) merge(l4[j], v4[j]);
   }
   for (; i < ns; i++) {
     const size_t sp = (size_t)(base + i);
-    merge(a.ws_plse[sp * kMaxUnitRows + r],
-          *reinterpret_cast<const f32x4*>(a.ws_po + sp * (kMaxUnitRows * kDC) + frag));
+    merge(a.ws_plse[sp * a.split_rows + r],
+          *reinterpret_cast<const f32x4*>(a.ws_po + sp * ((size_t)a.split_rows * kDC) + frag));
   }
   if (ns == 0 || mx == kNegInf) {
     *reinterpret_cast<u32x2*>(dst) = u32x2{0u, 0u};
@@ -1323,9 +1324,9 @@ WsLayout ws_layout(const Geometry& g) {
   w.meta = off;
   off = up(off + sizeof(int32_t) * 4 * (size_t)g.n_units);
   w.plse = off;
-  off = up(off + sizeof(float) * (size_t)g.max_splits * kMaxUnitRows);
+  off = up(off + sizeof(float) * (size_t)g.max_splits * g.split_rows);
   w.po = off;
-  off = up(off + sizeof(float) * (size_t)g.max_splits * kMaxUnitRows * kDC);
+  off = up(off + sizeof(float) * (size_t)g.max_splits * g.split_rows * kDC);
   w.zero = off;
   off = up(off + 1280);
   w.total = off;

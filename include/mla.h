@@ -131,6 +131,29 @@ mla_status mla_decode(const void *q_nope, const void *q_rope, const void *kv_pag
                       hipStream_t stream);
 
 /*
+ * mla_decode without a caller-supplied workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The split workspace is a static device
+ * array inside the library, MLA_NOALLOC_SCRATCH_BYTES (96 MiB) per device,
+ * which the library holds on every device it runs on until the process
+ * ends.  Arguments and results are those of mla_decode (which always plans:
+ * there is no `planned`); nothing is allocated or freed.  A request whose
+ * workspace (mla_workspace_size with topk = 0) exceeds the array returns
+ * MLA_ERR_WORKSPACE before anything is enqueued; the dense named workloads
+ * fit on a 256-CU device with num_wg = 0.  Every call on one device shares
+ * that device's array: calls whose executions overlap on one device (on
+ * different streams, or from different threads) race and give undefined
+ * results; calls ordered on one stream are safe.
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES (96u * 1024u * 1024u)
+mla_status mla_decode_noalloc(const void *q_nope, const void *q_rope, const void *kv_pages,
+                              const float *kv_scales, mla_kv_dtype kv_dtype, int num_pages,
+                              const int32_t *block_table, int bt_stride,
+                              const int32_t *cache_seqlens, int B, int Sq, int H,
+                              float softmax_scale, int causal, void *out, float *lse, int num_wg,
+                              hipStream_t stream);
+
+/*
  * Sparse (DSA top-k) absorbed MLA decode: query (b, s) attends over the
  * positions indices[b, s, 0..topk) (see "Visibility" above).  Arguments as
  * mla_decode, plus indices and topk (>= 1); there is no causal rule.  Each

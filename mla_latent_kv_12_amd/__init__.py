@@ -31,7 +31,7 @@ STATUS = ["MLA_OK", "MLA_ERR_NULL", "MLA_ERR_SHAPE", "MLA_ERR_UNSUPPORTED", "MLA
           "MLA_ERR_WORKSPACE", "MLA_ERR_HIP"]
 EXPORTS = ["mla_workspace_size", "mla_plan", "mla_decode", "mla_sparse_decode", "mla_attend",
            "mla_combine", "mla_kv_append", "mla_dsa_select", "mla_absorb_query", "mla_project_out",
-           "mla_prefill", "mla_status_str", "mla_last_error"]
+           "mla_prefill", "mla_decode_noalloc", "mla_status_str", "mla_last_error"]
 
 _lib = None
 
@@ -74,6 +74,9 @@ def lib():
         for fn in (L.mla_absorb_query, L.mla_project_out):
             fn.restype = i32
             fn.argtypes = [vp, vp, vp, i32, i32, vp]
+        L.mla_decode_noalloc.restype = i32
+        L.mla_decode_noalloc.argtypes = [vp, vp, vp, vp, i32, i32, vp, i32, vp, i32, i32, i32,
+                                         f32, i32, vp, vp, i32, vp]
         L.mla_prefill.restype = i32
         L.mla_prefill.argtypes = [vp, vp, vp, i32, i32, i32, f32, i32, vp, vp, vp]
         L.mla_status_str.restype = ctypes.c_char_p
@@ -149,6 +152,8 @@ def _common(q_nope, q_rope, kv_pages, kv_scales, block_table, cache_seqlens, out
     _req(lse, "lse", (torch.float32,), 3)
     if tuple(out.shape) != (B, Sq, H, 512) or tuple(lse.shape) != (B, Sq, H):
         raise ValueError("out must be [B,Sq,H,512] and lse [B,Sq,H]")
+    if workspace is False:      # the call brings its own workspace
+        return B, Sq, H, fp8, out, lse, None
     if workspace is None:
         workspace = alloc_workspace(B, Sq, H, topk, num_wg, dev)
     _req(workspace, "workspace", (torch.uint8,), 1)
@@ -175,6 +180,21 @@ def decode(q_nope, q_rope, kv_pages, block_table, cache_seqlens, softmax_scale, 
         kv_pages.shape[0], block_table.data_ptr(), block_table.shape[1], cache_seqlens.data_ptr(),
         B, Sq, H, float(softmax_scale), int(bool(causal)), out.data_ptr(), lse.data_ptr(),
         workspace.data_ptr(), workspace.numel(), int(num_wg), int(bool(planned)), _stream(q_nope)))
+    return out, lse
+
+
+def decode_noalloc(q_nope, q_rope, kv_pages, block_table, cache_seqlens, softmax_scale,
+                   kv_scales=None, causal=False, out=None, lse=None, num_wg=0):
+    """mla_decode_noalloc: mla_decode with the library's static workspace
+    (nothing allocated on the device if out and lse are given)."""
+    B, Sq, H, fp8, out, lse, _ = _common(q_nope, q_rope, kv_pages, kv_scales, block_table,
+                                         cache_seqlens, out, lse, False, 0, num_wg)
+    _check(lib().mla_decode_noalloc(
+        q_nope.data_ptr(), q_rope.data_ptr(), kv_pages.data_ptr(),
+        kv_scales.data_ptr() if fp8 else None, MLA_KV_FP8_E4M3 if fp8 else MLA_KV_BF16,
+        kv_pages.shape[0], block_table.data_ptr(), block_table.shape[1], cache_seqlens.data_ptr(),
+        B, Sq, H, float(softmax_scale), int(bool(causal)), out.data_ptr(), lse.data_ptr(),
+        int(num_wg), _stream(q_nope)))
     return out, lse
 
 

@@ -181,3 +181,19 @@ def test_projections_reject_before_launch(fn, args, code):
 def test_prefill_rejects_before_launch(args, code):
     assert mla.lib().mla_prefill(*args, None) == code
     assert mla.lib().mla_last_error().decode() != ""
+
+
+def test_decode_noalloc_rejects_requests_beyond_its_scratch():
+    L = mla.lib()
+    f = lambda B, H, num_wg: L.mla_decode_noalloc(FAKE, FAKE, FAKE, None, 0, 10, FAKE, 4, FAKE, B,
+                                                  1, H, 0.1, 0, FAKE, FAKE, num_wg, None)
+    # 4096 workgroups over 64 sequences of 128 rows: about 1 GB of split partials
+    assert mla.workspace_size(64, 1, 128, 0, 4096) > 96 * 1024 * 1024
+    assert f(64, 128, 4096) == WS
+    assert "MLA_NOALLOC_SCRATCH_BYTES" in L.mla_last_error().decode()
+    assert f(64, 128, 1 << 20) == SHAPE
+    assert f(0, 128, 8) == SHAPE
+    # the named dense workloads fit at one workgroup per CU of a 256-CU device
+    assert mla.workspace_size(64, 1, 128, 0, 256) <= 96 * 1024 * 1024
+    assert mla.workspace_size(4, 1, 128, 0, 256) <= 96 * 1024 * 1024
+    assert mla.workspace_size(128, 2, 16, 0, 1024) <= 96 * 1024 * 1024

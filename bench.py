@@ -1,18 +1,26 @@
 """Benchmark of the weight-absorbed MLA decode path on one MI355X.
 
-One step = one full decode of the workload through the C ABI: the split-KV
-scheduling pass (mla_plan), the main pass (mla_attend) and the split merge
-(mla_combine), over inputs already resident in HBM.  Steps rotate over
-several copies of the latent cache so consecutive steps do not find it in
-the 256 MB last-level cache.  `--graph` times replays of the three calls
-captured as one HIP graph per cache copy instead of plain stream launches
-(the calls never allocate or synchronise, so they capture as they are; on
-MI355X this measured the same step time).
+One step = one full decode of the workload through the C ABI: a single
+mla_decode (mla_sparse_decode) call, which enqueues the split-KV scheduling
+pass, the main pass and the split merge, over inputs already resident in
+HBM.  Steps rotate over several copies of the latent cache so consecutive
+steps do not find it in the 256 MB last-level cache.  Steps are timed as
+replays of one HIP graph per cache copy holding that call, the way a serving
+loop runs a graph-capturable decode: Python argument checks per call take
+longer than the smaller workloads' GPU time, so plain stream launches from
+Python (also reported) can leave the GPU waiting.  Events sit only around
+the timed loop.  The main kernel is timed from back-to-back single-kernel
+graph replays with an event between consecutive ones.  Before any timed
+loop, steps run for --settle-s seconds: the GPU's clocks settle only under
+sustained work.
 
 Prints one JSON line.  `value` is algorithmic TFLOP/s of the whole step;
 `roofline` describes the main kernel (mla_attend) timed with HIP events on
-the stream it runs on; `cpu_baseline` is the CPU oracle timed on a bounded
-sample of the same workload on this host.
+the stream it runs on (mean, as rocprofv3 reports it; also p10/median/p90
+and the median per cache copy); `roofline_step` is the same algorithmic
+bytes over the whole step; `cpu_baseline` is the CPU oracle timed on a
+bounded sample of the same workload on this host's cores available to the
+job.
 
 Algorithmic work (per query row and visible token): 2*576 FLOP for the
 score and 2*512 for the output, 2176 in all; bytes: every visible cached
@@ -88,9 +96,21 @@ def measured_traffic(workload: str):
     return d.get("hbm_bytes_per_launch")
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(inp, target_s: float):
     import oracle
-    cores = min(os.cpu_count() or 1, int(os.environ.get("OMP_NUM_THREADS", "16") or 16), 16)
+    # every core this job may use: OMP_NUM_THREADS when the host sets it (the
+    # CPU share a job gets), else the process's affinity set
+    cores = oracle.default_threads()
     H, Sq = inp["H"], inp["Sq"]
     vis = visible_counts(inp)                     # [B, Sq]
     per_row_flop = np.repeat(vis.reshape(-1), H) * FLOP_PER_ROW_TOKEN
@@ -106,9 +126,35 @@ def cpu_baseline(inp, target_s: float):
     oracle.decode(inp, rows=range(n), nthreads=cores)
     dt = time.perf_counter() - t0
     flop = float(per_row_flop[:n].sum())
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = None
     return {"value": round(flop / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
             "kind": "oracle", "seconds": round(dt, 2),
-            "sample": f"first {n} of {per_row_flop.size} query rows (all their visible tokens), fp64"}
+            "sample": f"first {n} of {per_row_flop.size} query rows (all their visible tokens), fp64",
+            "nproc": os.cpu_count(), "affinity_cpus": affinity,
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS"), "cpu_model": cpu_model()}
+
+
+def settle(fn, seconds: float):
+    """Runs fn(k) until `seconds` of wall time have passed (untimed)."""
+    t0 = time.perf_counter()
+    k = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(20):
+            fn(k)
+            k += 1
+        torch.cuda.synchronize()
+
+
+def main_kernel_name(inp) -> str:
+    """Name of the main-pass kernel the library launches for this input."""
+    rows = inp["H"] if inp["indices"] is not None else inp["Sq"] * inp["H"]
+    rows = min(rows, 128)
+    shape = "r4" if rows > 64 else "r2" if rows > 32 else "r1w"
+    kind = "sparse" if inp["indices"] is not None else "dense"
+    return f"decode_{'fp8' if inp['kv_dtype'] == 'fp8' else 'bf16'}_{kind}_{shape}"
 
 
 def bench_append(args):
@@ -289,9 +335,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="dsv3_decode", choices=list(S.CONFIGS))
     ap.add_argument("--copies", type=int, default=3, help="cache copies rotated over steps")
+    ap.add_argument("--settle-s", type=float, default=0.5,
+                    help="seconds of untimed steps before the warmup steps (clock settling)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--graph", action="store_true", help="time HIP graph replays of the step")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run plain 1 GiB device copies (calibrates HBM byte counters)")
     ap.add_argument("--op", default="decode", choices=["decode", "append", "select", "absorb", "project", "prefill"],
@@ -343,69 +390,110 @@ def main():
     out = torch.empty((B, Sq, H, 512), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((B, Sq, H), dtype=torch.float32, device=dev)
 
-    def step(k, ev=None):
+    def step(k):
+        """One decode step: a single C-ABI call that enqueues the scheduling
+        pass, the main pass and the combine."""
         i = k % args.copies
-        mla.plan(g["cache_seqlens"], B, Sq, H, ws, topk=topk)
-        if ev is not None:
-            ev[0].record()
+        if topk:
+            mla.sparse_decode(g["q_nope"], g["q_rope"], kvs[i], g["block_table"],
+                              g["cache_seqlens"], g["indices"], g["softmax_scale"],
+                              kv_scales=scs[i], out=out, lse=lse, workspace=ws)
+        else:
+            mla.decode(g["q_nope"], g["q_rope"], kvs[i], g["block_table"], g["cache_seqlens"],
+                       g["softmax_scale"], kv_scales=scs[i], causal=g["causal"], out=out,
+                       lse=lse, workspace=ws)
+
+    def attend(k):
+        i = k % args.copies
         mla.attend(g["q_nope"], g["q_rope"], kvs[i], g["block_table"], g["cache_seqlens"],
                    g["softmax_scale"], ws, kv_scales=scs[i], indices=g["indices"],
                    causal=g["causal"], out=out, lse=lse)
-        if ev is not None:
-            ev[1].record()
-        mla.combine(g["cache_seqlens"], B, Sq, H, out, lse, ws, topk=topk)
 
-    for k in range(args.warmup):
-        step(k)
-    torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record()
-    for k in range(args.steps):
-        step(k, evs[k])
-    t_end.record()
-    torch.cuda.synchronize()
-    ms_eager = t_start.elapsed_time(t_end) / args.steps
-    attend_all = np.array([a.elapsed_time(b) for a, b in evs])
-    attend_ms = float(attend_all.mean())
-    assert torch.isfinite(lse).all(), "non-finite lse"
-    ms = ms_eager
 
-    # The same steps with the scheduling pass run once and reused (a decode
-    # step runs mla_plan once for all its layers): main pass + combine.
-    mla.plan(g["cache_seqlens"], B, Sq, H, ws, topk=topk)
-    torch.cuda.synchronize()
-    t_start.record()
-    for k in range(args.steps):
-        i = k % args.copies
-        mla.attend(g["q_nope"], g["q_rope"], kvs[i], g["block_table"], g["cache_seqlens"],
-                   g["softmax_scale"], ws, kv_scales=scs[i], indices=g["indices"],
-                   causal=g["causal"], out=out, lse=lse)
-        mla.combine(g["cache_seqlens"], B, Sq, H, out, lse, ws, topk=topk)
-    t_end.record()
-    torch.cuda.synchronize()
-    ms_planned = t_start.elapsed_time(t_end) / args.steps
-    if args.graph:
-        # One graph per cache copy; replayed in the same rotation.
+    def timed(fn):
+        """Mean ms per call of fn(k) over args.steps calls, events only
+        around the whole loop."""
+        torch.cuda.synchronize()
+        t_start.record()
+        for k in range(args.steps):
+            fn(k)
+        t_end.record()
+        torch.cuda.synchronize()
+        return t_start.elapsed_time(t_end) / args.steps
+
+    def capture(fn):
+        """One HIP graph per cache copy holding fn(copy); the library's calls
+        never allocate or synchronise, so they capture as they are."""
         graphs = []
         for i in range(args.copies):
             gr = torch.cuda.CUDAGraph()
             with torch.cuda.graph(gr):
-                step(i)
+                fn(i)
             graphs.append(gr)
-        for k in range(args.warmup):
-            graphs[k % args.copies].replay()
         torch.cuda.synchronize()
-        t_start.record()
-        for k in range(args.steps):
-            graphs[k % args.copies].replay()
-        t_end.record()
-        torch.cuda.synchronize()
-        ms = t_start.elapsed_time(t_end) / args.steps
-        assert torch.isfinite(lse).all(), "non-finite lse"
+        return lambda k: graphs[k % args.copies].replay()
+
+    # Graphs: a whole step (plan + main + combine), the main pass alone (on a
+    # plan computed before capture) and main + combine (plan reused).
+    for k in range(args.copies):
+        step(k)
+    torch.cuda.synchronize()
+    g_step = capture(step)
+    mla.plan(g["cache_seqlens"], B, Sq, H, ws, topk=topk)
+    torch.cuda.synchronize()
+    g_attend = capture(attend)
+
+    def planned(k):
+        attend(k)
+        mla.combine(g["cache_seqlens"], B, Sq, H, out, lse, ws, topk=topk)
+
+    g_planned = capture(planned)
+
+    # The GPU's clocks settle only after some sustained work: the first loop
+    # a process times ran ~15% slower than the same loop repeated.  Steps for
+    # at least --settle-s seconds go first, then the --warmup steps.
+    settle(g_step, args.settle_s)
+    for k in range(args.warmup):
+        g_step(k)
+    ms = timed(g_step)
+    assert torch.isfinite(lse).all(), "non-finite lse"
+    # the same step as plain stream launches from Python (one mla_decode call
+    # per step); host-side argument checks can leave the GPU waiting here
+    for k in range(args.warmup):
+        step(k)
+    ms_eager = timed(step)
+    ms_planned = timed(g_planned)
+
+    # The main kernel on its own: one graph holding 4 * copies back-to-back
+    # launches (the cache copies in rotation), events only around its
+    # replays; the mean per launch is what a kernel trace averages.  Event
+    # pairs around single launches measured ~20 us longer per launch than the
+    # trace, so they only give the spread (p10/median/p90, per cache copy).
+    per = 4 * args.copies
+    many = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(many):
+        for j in range(per):
+            attend(j)
+    reps = max(1, args.steps // per)
+    for k in range(2):
+        many.replay()
+    torch.cuda.synchronize()
+    t_start.record()
+    for k in range(reps):
+        many.replay()
+    t_end.record()
+    torch.cuda.synchronize()
+    attend_ms = t_start.elapsed_time(t_end) / (reps * per)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for k in range(args.steps):
+        evs[k][0].record()
+        g_attend(k)
+        evs[k][1].record()
+    torch.cuda.synchronize()
+    attend_all = np.array([a.elapsed_time(b) for a, b in evs])
 
     tflops = flop / (ms * 1e-3) / 1e12
     achieved_gbs = nbytes / (attend_ms * 1e-3) / 1e9
@@ -419,10 +507,19 @@ def main():
         roof = {"bound": "mfma", "achieved": round(a_tf, 2), "peak": MFMA_BF16_PEAK_TFS,
                 "unit": "TFLOP/s", "frac": round(a_tf / MFMA_BF16_PEAK_TFS, 4)}
     roof["traffic"] = measured_traffic(args.workload)
-    roof["kernel"] = "mla_attend (decode_*_r4 / r2 / r1w)"
+    roof["kernel"] = main_kernel_name(inp)
     roof["kernel_ms"] = round(attend_ms, 5)
-    roof["kernel_ms_p10_median_p90"] = [round(float(np.percentile(attend_all, q)), 5) for q in (10, 50, 90)]
+    # spread of single launches (event pairs: each ~20 us above the trace)
+    roof["single_launch_ms_p10_median_p90"] = [round(float(np.percentile(attend_all, q)), 5) for q in (10, 50, 90)]
+    # median single-launch time per cache copy (steps k, k + copies, ...)
+    roof["single_launch_ms_median_per_cache_copy"] = [
+        round(float(np.median(attend_all[i::args.copies])), 5) for i in range(args.copies)]
     roof["mfma_frac"] = round(flop / (attend_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS, 4)
+    # the same algorithmic bytes over the whole step (plan + main pass +
+    # combine, as launched), the figure `value` is quoted on
+    step_gbs = nbytes / (ms * 1e-3) / 1e9
+    roof_step = {"bound": roof["bound"], "achieved": round(step_gbs, 1), "peak": HBM_PEAK_GBS,
+                 "unit": "GB/s", "frac": round(step_gbs / HBM_PEAK_GBS, 4)}
 
     res = {
         "metric": "MLA absorbed decode TFLOPS + HBM GB/s (% roofline), B=64 H=128 L~8K",
@@ -433,12 +530,13 @@ def main():
         "config": {"workload": args.workload, "B": B, "Sq": Sq, "H": H,
                    "tokens": int(inp["cache_seqlens"].sum()), "kv": inp["kv_dtype"],
                    "topk": topk, "seed": inp["seed"], "cache_copies": args.copies,
-                   "launch": "hip_graph" if args.graph else "stream"},
+                   "launch": "hip_graph"},
         "ms_per_step_stream_launch": round(ms_eager, 5),
         "ms_per_step_plan_reused": round(ms_planned, 5),
         "gbps_step": round(nbytes / (ms * 1e-3) / 1e9, 1),
         "alg_bytes": nbytes, "alg_flop": flop,
         "roofline": roof,
+        "roofline_step": roof_step,
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)

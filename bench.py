@@ -8,8 +8,10 @@ steps do not find it in the 256 MB last-level cache.  Steps are timed as
 replays of one HIP graph per cache copy holding that call, the way a serving
 loop runs a graph-capturable decode: Python argument checks per call take
 longer than the smaller workloads' GPU time, so plain stream launches from
-Python (also reported) can leave the GPU waiting.  Events sit only around
-the timed loop.  The main kernel is timed from back-to-back single-kernel
+Python (also reported) can leave the GPU waiting.  Each replay runs one step
+per cache copy back to back, as a serving loop's graph holds many layers'
+calls; one step per replay is reported too.  Events sit only around the
+timed loop.  The main kernel is timed from back-to-back single-kernel
 graph replays with an event between consecutive ones.  Before any timed
 loop, steps run for --settle-s seconds: the GPU's clocks settle only under
 sustained work.
@@ -79,19 +81,24 @@ def algorithmic(inp):
     return flop, nbytes
 
 
-def kernel_source_sha() -> str:
-    p = os.path.join(ROOT, "mla_latent_kv_12_amd", "csrc", "mla_kernels.hip")
+def kernel_source_sha(inp=None) -> str:
+    """First 16 hex of the SHA-256 of the source file holding the main
+    kernel for `inp` (the head-group sparse kernel has a file of its own)."""
+    name = "mla_kernels.hip"
+    if inp is not None and main_kernel_name(inp).endswith("_hg"):
+        name = "mla_sparse.hip"
+    p = os.path.join(ROOT, "mla_latent_kv_12_amd", "csrc", name)
     return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
+def measured_traffic(workload: str, inp=None):
     """HBM bytes per main-kernel launch from the committed counter summary,
     or None when there is none or the kernel source changed since."""
     p = os.path.join(ROOT, "profiles", f"traffic_attend_{workload}.json")
     if not os.path.exists(p):
         return None
     d = json.load(open(p))
-    if d.get("kernel_sha") != kernel_source_sha():
+    if d.get("kernel_sha") != kernel_source_sha(inp):
         return None
     return d.get("hbm_bytes_per_launch")
 
@@ -150,6 +157,8 @@ def settle(fn, seconds: float):
 
 def main_kernel_name(inp) -> str:
     """Name of the main-pass kernel the library launches for this input."""
+    if inp["indices"] is not None and inp["kv_dtype"] != "fp8":
+        return "decode_bf16_sparse_hg"   # head-group kernel: the whole sparse step
     rows = inp["H"] if inp["indices"] is not None else inp["Sq"] * inp["H"]
     rows = min(rows, 128)
     shape = "r4" if rows > 64 else "r2" if rows > 32 else "r1w"
@@ -441,6 +450,14 @@ def main():
         step(k)
     torch.cuda.synchronize()
     g_step = capture(step)
+    # a serving loop holds many layers' decode calls in one graph: each
+    # replay of g_steps runs `copies` consecutive steps (one per cache
+    # copy), which share the replay's launch the same way
+    g_steps = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_steps):
+        for i in range(args.copies):
+            step(i)
+    torch.cuda.synchronize()
     mla.plan(g["cache_seqlens"], B, Sq, H, ws, topk=topk)
     torch.cuda.synchronize()
     g_attend = capture(attend)
@@ -457,7 +474,15 @@ def main():
     settle(g_step, args.settle_s)
     for k in range(args.warmup):
         g_step(k)
-    ms = timed(g_step)
+    n_rep = max(1, args.steps // args.copies)
+    torch.cuda.synchronize()
+    t_start.record()
+    for k in range(n_rep):
+        g_steps.replay()
+    t_end.record()
+    torch.cuda.synchronize()
+    ms = t_start.elapsed_time(t_end) / (n_rep * args.copies)
+    ms_one_per_graph = timed(g_step)
     assert torch.isfinite(lse).all(), "non-finite lse"
     # the same step as plain stream launches from Python (one mla_decode call
     # per step); host-side argument checks can leave the GPU waiting here
@@ -506,7 +531,7 @@ def main():
         a_tf = flop / (attend_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(a_tf, 2), "peak": MFMA_BF16_PEAK_TFS,
                 "unit": "TFLOP/s", "frac": round(a_tf / MFMA_BF16_PEAK_TFS, 4)}
-    roof["traffic"] = measured_traffic(args.workload)
+    roof["traffic"] = measured_traffic(args.workload, inp)
     roof["kernel"] = main_kernel_name(inp)
     roof["kernel_ms"] = round(attend_ms, 5)
     # spread of single launches (event pairs: each ~20 us above the trace)
@@ -532,6 +557,7 @@ def main():
                    "topk": topk, "seed": inp["seed"], "cache_copies": args.copies,
                    "launch": "hip_graph"},
         "ms_per_step_stream_launch": round(ms_eager, 5),
+        "ms_per_step_one_step_per_graph": round(ms_one_per_graph, 5),
         "ms_per_step_plan_reused": round(ms_planned, 5),
         "gbps_step": round(nbytes / (ms * 1e-3) / 1e9, 1),
         "alg_bytes": nbytes, "alg_flop": flop,

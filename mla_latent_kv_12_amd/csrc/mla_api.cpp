@@ -62,6 +62,29 @@ bool make_geometry(int B, int Sq, int H, int topk, int num_wg, mla::Geometry* g)
   g->split_rows = g->m_unit > 64 ? 128 : g->m_unit > 32 ? 64 : 32;
   g->num_wg = num_wg;
   g->max_splits = num_wg + g->n_units;
+  g->hg_groups = g->hg_splits = g->hg_span = 0;
+  if (g->sparse) {
+    // Head-group sparse decode: items of 32 rows; an item's index list is
+    // split over up to kMaxHgSplits workgroups when there are fewer items
+    // than workgroups, keeping at least 16 entries per wave.
+    const long long items = n_su * (((long long)H + 31) / 32);
+    long long s = 1;
+    if (items < num_wg && items <= mla::kMaxHgSplitItems) {
+      s = (num_wg + items - 1) / items;
+      const long long by_len = ((long long)topk + 63) / 64;
+      if (s > by_len) s = by_len;
+      if (s > mla::kMaxHgSplits) s = mla::kMaxHgSplits;
+      if (s < 1) s = 1;
+    }
+    // entries per workgroup: a multiple of 64 (16 per wave); ranges past
+    // the list's end are dropped
+    const long long per_wg = ((((long long)topk + s - 1) / s) + 63) / 64 * 64;
+    s = ((long long)topk + per_wg - 1) / per_wg;
+    if (items * s > (1LL << 30)) return false;
+    g->hg_groups = (H + 31) / 32;
+    g->hg_splits = (int)s;
+    g->hg_span = (int)(per_wg / 4);
+  }
   return true;
 }
 
@@ -97,6 +120,9 @@ mla_status fill_sched_args(const mla::Geometry& g, const int32_t* seqlens, void*
   a->n_units = g.n_units;
   a->num_wg = g.num_wg;
   a->split_rows = g.split_rows;
+  a->hg_groups = g.hg_groups;
+  a->hg_splits = g.hg_splits;
+  a->hg_span = g.hg_span;
   return MLA_OK;
 }
 
@@ -157,12 +183,21 @@ mla_status mla::run_decode(const void* q_nope, const void* q_rope, const void* k
   a.scale_log2 = softmax_scale * 1.44269504088896340736f;
 
   hipError_t e;
+  const bool fp8 = kv_dtype == MLA_KV_FP8_E4M3;
+  if (mla::uses_hg(g, fp8)) {
+    // the attend stage produces finished rows: no scheduling or merge stage
+    if (stages & mla::kStageAttend) {
+      e = mla::launch_sparse_hg(g, a, stream);
+      if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+    }
+    return MLA_OK;
+  }
   if ((stages & mla::kStagePlan) && !planned) {
     e = mla::launch_plan(g, a, stream);
     if (e != hipSuccess) return fail(MLA_ERR_HIP, "plan launch: %s", hipGetErrorString(e));
   }
   if (stages & mla::kStageAttend) {
-    e = mla::launch_decode(g, a, kv_dtype == MLA_KV_FP8_E4M3, stream);
+    e = mla::launch_decode(g, a, fp8, stream);
     if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
   }
   if (stages & mla::kStageCombine) {

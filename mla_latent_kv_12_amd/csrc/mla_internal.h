@@ -42,7 +42,15 @@ struct Geometry {
   int split_rows;  // rows of one split partial: 32 * waves of the kernel shape (32, 64, 128)
   int num_wg;      // persistent workgroups
   int max_splits;  // num_wg + n_units
+  // Sparse bf16 decode by head group: 32-row groups per sequence unit, index
+  // ranges per group (one workgroup each) and index entries per wave.
+  int hg_groups, hg_splits, hg_span;
 };
+
+// The head-group sparse decode splits an item's index list over at most this
+// many workgroups, and only when there are fewer items than this bound.
+constexpr int kMaxHgSplits = 8;
+constexpr int kMaxHgSplitItems = 4096;
 
 struct WsLayout {
   size_t work;   // int32 [(num_wg + 1) * 2]   (first unit, first tile) per WG
@@ -78,6 +86,7 @@ struct DecodeArgs {
   int n_su, m_full, row_blocks, n_units, num_wg, split_rows;
   int causal;
   float scale_log2;  // softmax_scale * log2(e)
+  int hg_groups, hg_splits, hg_span;
 };
 
 // Cache append: the Sq new latent rows of every sequence into their slots.
@@ -142,5 +151,10 @@ mla_status fail_status(mla_status s, const char* msg);
 hipError_t launch_plan(const Geometry& g, const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode(const Geometry& g, const DecodeArgs& a, bool fp8, hipStream_t stream);
 hipError_t launch_combine(const Geometry& g, const DecodeArgs& a, hipStream_t stream);
+// Sparse decode of a bf16 cache by head group (mla_sparse.hip): the main
+// kernel, and when index lists are split over workgroups the merge of their
+// partials; no scheduling pass.
+hipError_t launch_sparse_hg(const Geometry& g, const DecodeArgs& a, hipStream_t stream);
+inline bool uses_hg(const Geometry& g, bool fp8) { return g.sparse && !fp8; }
 
 }  // namespace mla

@@ -241,6 +241,60 @@ def test_sparse_all_invalid_gives_empty():
     full_check(inp)
 
 
+def sparse_case(B, H, lens, topk, seed, kv="bf16", holes=True):
+    """Random distinct selections per (b, s) (fewer than topk where a
+    sequence is short: the tail is -1), with some entries past the length."""
+    inp = custom(B=B, Sq=1, H=H, lens=lens, kv=kv, seed=seed)
+    g_ = torch.Generator().manual_seed(seed + 1)
+    ix = torch.full((B, 1, topk), -1, dtype=torch.int32)
+    for b, L in enumerate(lens):
+        n = min(topk, L)
+        ix[b, 0, :n] = torch.randperm(L, generator=g_)[:n].to(torch.int32)
+        if holes and n > 40:
+            ix[b, 0, 7] = L + 3          # past the length: invisible
+            ix[b, 0, n // 2] = -1        # a hole mid-list
+    inp["indices"] = ix
+    inp["topk"] = topk
+    return inp
+
+
+def test_sparse_long_lists_per_wave():
+    """topk 2048 on one workgroup per head group (num_wg=1): each wave walks
+    512 entries, four rounds of index and page lookups."""
+    full_check(sparse_case(2, 128, (5000, 2100), 2048, seed=41), num_wg=1)
+
+
+@pytest.mark.parametrize("num_wg", [1, 8, 64, 256, 4096])
+def test_sparse_index_ranges_per_head_group(num_wg):
+    """The same lists cut into 1..8 ranges merged by the last workgroup."""
+    full_check(sparse_case(2, 128, (3000, 1500), 1024, seed=42), num_wg=num_wg)
+
+
+def test_sparse_workspace_shared_across_shapes_and_garbage():
+    """One workspace, filled with random bytes first, shared by calls of
+    different shapes and range counts in turn: every call matches the
+    oracle and repeats bit for bit (the merge order is fixed)."""
+    m = mla()
+    a_in = sparse_case(2, 128, (3000, 1500), 1024, seed=43)
+    b_in = sparse_case(3, 64, (700, 2000, 1200), 512, seed=44)
+    ga, gb = dev(a_in), dev(b_in)
+    size = max(m.workspace_size(2, 1, 128, 1024, 4096), m.workspace_size(3, 1, 64, 512, 64),
+               m.workspace_size(2, 1, 128, 1024, 0))
+    ws = torch.randint(-128, 128, (size,), dtype=torch.int8, device="cuda").view(torch.uint8)
+    ref_a, ref_b = oracle.decode(a_in), oracle.decode(b_in)
+    first = {}
+    for rep in range(3):
+        for key, g, nw, ref, inp in (("a8", ga, 4096, ref_a, a_in), ("b", gb, 64, ref_b, b_in),
+                                     ("a2", ga, 0, ref_a, a_in)):
+            out, lse = run(g, num_wg=nw, workspace=ws)
+            torch.cuda.synchronize()
+            if rep == 0:
+                check(out, lse, ref[0], ref[1], f"{key} rep {rep}", nvis=visible_counts(inp))
+                first[key] = (out.clone(), lse.clone())
+            else:
+                assert torch.equal(out, first[key][0]) and torch.equal(lse, first[key][1]), f"{key} rep {rep}"
+
+
 # ---------------------------------------------------------------- a table row shorter than the sequence
 @pytest.mark.parametrize("kv", ["bf16", "fp8"])
 def test_tokens_past_the_table_row_are_invisible_dense(kv):

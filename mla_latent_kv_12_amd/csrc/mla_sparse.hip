@@ -126,13 +126,17 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_sparse_hg(DecodeArgs a) {
   // A selected entry names a token of sequence b; it is visible when it is
   // below the sequence length and its page lies inside the block-table row
   // and the pool.  Token rows are page * 64 + (index & 63), or -1.
+  // (loads from clamped, always valid addresses with the selects after
+  // them: a load under a branch makes the compiler wait for it there)
   auto load_idx = [&](int e0, int& i0, int& i1) __attribute__((always_inline)) {
     const int ea = e0 + lane, eb = ea + 64;
-    i0 = ea < e_hi ? idx_row[ea] : -1;
-    i1 = eb < e_hi ? idx_row[eb] : -1;
+    const int va = idx_row[min(ea, e_hi - 1)], vb = idx_row[min(eb, e_hi - 1)];
+    i0 = ea < e_hi ? va : -1;
+    i1 = eb < e_hi ? vb : -1;
   };
   auto load_pg = [&](int i) __attribute__((always_inline)) -> int {
-    return (i >= 0 && i < L && (i >> 6) < a.bt_stride) ? bt_row[i >> 6] : -1;
+    const int v = bt_row[min(max(i >> 6, 0), a.bt_stride - 1)];
+    return (i >= 0 && i < L && (i >> 6) < a.bt_stride) ? v : -1;
   };
   auto tok_of = [&](int i, int pg) __attribute__((always_inline)) -> int {
     const bool ok = i >= 0 && i < L && (i >> 6) < a.bt_stride && pg >= 0 && pg < a.num_pages;
@@ -199,30 +203,57 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_sparse_hg(DecodeArgs a) {
   if (nch > 0) {
     // Round 0 lookups and the query rows (loads in this order, so that the
     // page lookups wait only for the index loads).
-    int i0, i1;
-    load_idx(e_lo, i0, i1);
+    // The block-table row is fetched towards L2 beside the index loads (into
+    // a scratch area of LDS), so the dependent page lookups find it there.
+    {
+      const int nb = min(a.bt_stride, 1024);  // entries: up to 4 KB per row
+#pragma unroll
+      for (int k = 0; k < 4; k++) {
+        const int e = 256 * k + 64 * w + lane;
+        if (e < nb) copy4_v(bt_row + e, lds_addr(lds + Y::kLookOff + w * 1024 + k * 256));
+      }
+    }
+    // Issue order: index entries, their pages, then the query rows (vector
+    // loads retire in order, so the page lookups wait only for the index
+    // loads, and the query rows stay in flight while the pages are
+    // awaited).  The empty asm statements with a memory clobber keep the
+    // compiler from reordering the three groups.
+    const int ea = e_lo + lane, eb = ea + 64;
+    const int va = idx_row[min(ea, e_hi - 1)], vb = idx_row[min(eb, e_hi - 1)];
+    asm volatile("" ::: "memory");
+    const int pa = bt_row[min(max(va >> 6, 0), a.bt_stride - 1)];
+    const int pbg = bt_row[min(max(vb >> 6, 0), a.bt_stride - 1)];
+    asm volatile("" ::: "memory");
     {
       const int r16 = lane & 15, g4 = lane >> 4;
 #pragma unroll
       for (int rb = 0; rb < 2; rb++) {
+        // rows past the head count score with row 0's query; they are
+        // never written out
         const int r = 16 * rb + r16;
-        const bool ok = r < rows;
-        const size_t grow = row0 + (ok ? r : 0);
+        const size_t grow = row0 + (r < rows ? r : 0);
         const bf16x8* qn = reinterpret_cast<const bf16x8*>(a.q_nope + grow * kDC) + g4;
         const bf16x8* qr = reinterpret_cast<const bf16x8*>(a.q_rope + grow * kDR) + g4;
 #pragma unroll
-        for (int ks = 0; ks < 16; ks++) qf[rb][ks] = ok ? qn[4 * ks] : bf16x8{};
+        for (int ks = 0; ks < 16; ks++) qf[rb][ks] = qn[4 * ks];
 #pragma unroll
-        for (int ks = 0; ks < 2; ks++) qf[rb][16 + ks] = ok ? qr[4 * ks] : bf16x8{};
+        for (int ks = 0; ks < 2; ks++) qf[rb][16 + ks] = qr[4 * ks];
       }
     }
-    const int p0 = load_pg(i0), p1 = load_pg(i1);
-    t0 = tok_of(i0, p0);
-    t1 = tok_of(i1, p1);
+    asm volatile("" ::: "memory");
+    const int i0 = ea < e_hi ? va : -1, i1 = eb < e_hi ? vb : -1;
+    t0 = tok_of(i0, pa);
+    t1 = tok_of(i1, pbg);
     const Next d0 = setup(0, t0, t1);
     wait_lds();
 #pragma unroll
     for (int k = 0; k < Y::kTok + 2; k++) copy(k, d0);
+    // Take delivery of the query rows here (with chunk 0): a wait left to
+    // the compiler lands inside the loop, where it also waits for copies.
+#pragma unroll
+    for (int rb = 0; rb < 2; rb++)
+#pragma unroll
+      for (int ks = 0; ks < 18; ks++) asm volatile("" : "+v"(qf[rb][ks]));
   }
 
   // ------------------------------------------------------------ main loop
@@ -417,12 +448,14 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_sparse_hg(DecodeArgs a) {
   const float mown = stm[32 * w + r];
   const float f = (has && mown != kNegInf) ? __builtin_amdgcn_exp2f(mown - M) / Lsum : 0.f;
   const float lse2 = has ? M + __log2f(Lsum) : kNegInf;
+  // the weight goes into the values handed to other waves as they are
+  // stored, and into the owned quarter in place
 #pragma unroll
-  for (int i = 0; i < 16; i++) acc_scale(o[i], f);
+  for (int i = 0; i < 4; i++) acc_scale(o[i], f);
 
   // 4 slots from SB to `buf` (4 KB per slot, 1 KB of consecutive bytes per
   // store), or added from `buf` into slots 0..3
-  auto put4 = [&](auto SB, float* buf) __attribute__((always_inline)) {
+  auto put4 = [&](auto SB, float* buf, float sc) __attribute__((always_inline)) {
     constexpr int sb = decltype(SB)::value;
 #pragma unroll
     for (int jj = 0; jj < 4; jj++)
@@ -430,7 +463,7 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_sparse_hg(DecodeArgs a) {
       for (int q = 0; q < 4; q++)
         *reinterpret_cast<f32x4*>(buf + (jj * 4 + q) * 256 + lane * 4) =
             f32x4{acc_get(o[sb + jj], 4 * q), acc_get(o[sb + jj], 4 * q + 1), acc_get(o[sb + jj], 4 * q + 2),
-                  acc_get(o[sb + jj], 4 * q + 3)};
+                  acc_get(o[sb + jj], 4 * q + 3)} * sc;
   };
   auto add4 = [&](const float* buf, float keep, float wt) __attribute__((always_inline)) {
 #pragma unroll
@@ -446,7 +479,7 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_sparse_hg(DecodeArgs a) {
   unroll<3>([&](auto K) __attribute__((always_inline)) {
     constexpr int k = decltype(K)::value + 1;
     float* const reg = X + ((k & 1) ? 0 : 16384);
-    put4(std::integral_constant<int, 4 * k>{}, reg + 4096 * ((w + k) & 3));
+    put4(std::integral_constant<int, 4 * k>{}, reg + 4096 * ((w + k) & 3), f);
     __syncthreads();
     add4(reg + 4096 * w, 1.f, 1.f);
   });
@@ -477,7 +510,7 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_sparse_hg(DecodeArgs a) {
   // Several ranges: store this range's normalised partial (each wave its
   // quarter, in fragment order) and its log2-sum-exp; combine_hg merges them.
   const size_t part = (size_t)item * S + split;
-  put4(std::integral_constant<int, 0>{}, a.ws_po + part * (16 * 1024) + w * 4096);
+  put4(std::integral_constant<int, 0>{}, a.ws_po + part * (16 * 1024) + w * 4096, 1.f);
   if (w == 0 && lane < 32) a.ws_plse[part * 32 + r] = lse2;
 }
 

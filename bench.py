@@ -296,6 +296,103 @@ def bench_proj(args):
     }), flush=True)
 
 
+def bench_layer(args):
+    """Times the whole absorbed decode layer on a dense workload as
+    mla_decode_layer (absorption with the schedule in the same launch, main
+    pass, merge, projection: four launches) against the same computation as
+    separate calls (mla_absorb_query,
+    mla_decode -- schedule, main pass, merge -- and mla_project_out), both as
+    graph replays of one layer per cache copy, random N(0, 1/512) weights.
+    Algorithmic bytes: every cached token once, q_c, q_rope, o and lse per
+    row, and both weight tensors once; FLOP: the decode's plus 2*128*512 per
+    row and head for each projection."""
+    import mla_latent_kv_12_amd as mla
+    dev = torch.device("cuda:0")
+    inp = S.make_inputs(S.config(args.workload), poison=False)
+    if inp["indices"] is not None:
+        raise SystemExit("--op layer runs dense workloads")
+    g = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    B, Sq, H = inp["B"], inp["Sq"], inp["H"]
+    M = B * Sq
+    gen = torch.Generator().manual_seed(98)
+    q_c = torch.randn((B, Sq, H, 128), generator=gen).to(torch.bfloat16).to(dev)
+    w_uk_t = (torch.randn((H, 512, 128), generator=gen) * 512 ** -0.5).to(torch.bfloat16).to(dev)
+    w_uv = (torch.randn((H, 128, 512), generator=gen) * 512 ** -0.5).to(torch.bfloat16).to(dev)
+    kvs = [g["kv_pages"]] + [g["kv_pages"].clone() for _ in range(args.copies - 1)]
+    scs = [g["kv_scales"]] * args.copies if g["kv_scales"] is None else \
+        [g["kv_scales"]] + [g["kv_scales"].clone() for _ in range(args.copies - 1)]
+    ws_layer = torch.empty(mla.layer_workspace_size(B, Sq, H), dtype=torch.uint8, device=dev)
+    ws = mla.alloc_workspace(B, Sq, H)
+    o = torch.empty((B, Sq, H, 128), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, Sq, H), dtype=torch.float32, device=dev)
+    q_nope = torch.empty((B, Sq, H, 512), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((B, Sq, H, 512), dtype=torch.bfloat16, device=dev)
+
+    def fused(i):
+        mla.decode_layer(q_c, w_uk_t, g["q_rope"], w_uv, kvs[i], g["block_table"], g["cache_seqlens"],
+                         g["softmax_scale"], kv_scales=scs[i], causal=g["causal"], o=o, lse=lse,
+                         workspace=ws_layer)
+
+    def separate(i):
+        mla.absorb_query(q_c, w_uk_t, out=q_nope)
+        mla.decode(q_nope, g["q_rope"], kvs[i], g["block_table"], g["cache_seqlens"], g["softmax_scale"],
+                   kv_scales=scs[i], causal=g["causal"], out=out, lse=lse, workspace=ws)
+        mla.project_out(out, w_uv, out=o)
+
+    def graph_of(fn):
+        for i in range(args.copies):
+            fn(i)
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            for i in range(args.copies):
+                fn(i)
+        torch.cuda.synchronize()
+        return gr
+
+    g_fused, g_sep = graph_of(fused), graph_of(separate)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < args.settle_s:
+        g_fused.replay()
+        torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n_rep = max(1, args.steps // args.copies)
+
+    def timed(gr):
+        for _ in range(max(1, args.warmup // args.copies)):
+            gr.replay()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(n_rep):
+            gr.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (n_rep * args.copies)
+
+    ms_sep = timed(g_sep)
+    ms = timed(g_fused)
+    ms_sep = min(ms_sep, timed(g_sep))   # order effects: each timed after the other once
+    dflop, _ = algorithmic(inp)
+    flop = dflop + 2 * 2.0 * M * H * 128 * 512
+    tokens = float(inp["cache_seqlens"].clamp(min=0).sum())
+    tok_bytes = 576 + 4 if inp["kv_dtype"] == "fp8" else 1152
+    nbytes = tokens * tok_bytes + M * H * (128 * 2 + 64 * 2 + 128 * 2 + 4) + 2 * H * 128 * 512 * 2
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "MLA absorbed decode layer (W_UK, decode, W_UV) TFLOP/s", "value": round(flop / (ms * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": n_rep * args.copies, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": args.workload, "op": "layer", "B": B, "Sq": Sq, "H": H,
+                   "cache_copies": args.copies, "launch": "hip_graph"},
+        "ms_per_step_separate_calls": round(ms_sep, 5), "speedup_vs_separate": round(ms_sep / ms, 4),
+        "launches_fused": 4, "launches_separate": 5,
+        "alg_bytes": nbytes, "alg_flop": flop,
+        "roofline_step": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": round(gbs / HBM_PEAK_GBS, 4)},
+    }), flush=True)
+
+
 def bench_prefill(args):
     """Times mla_prefill: causal MHA over decompressed per-head K/V, B=1,
     T=--prefill-len, H=128, d_qk 192, d_v 128, bf16 N(0,1).  FLOP: each of
@@ -350,9 +447,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run plain 1 GiB device copies (calibrates HBM byte counters)")
-    ap.add_argument("--op", default="decode", choices=["decode", "append", "select", "absorb", "project", "prefill"],
+    ap.add_argument("--op", default="decode",
+                    choices=["decode", "layer", "append", "select", "absorb", "project", "prefill"],
                     help="decode: the decode step (default); append: the cache append alone; "
                          "select: the DSA block top-k selection alone (sparse workloads); "
+                         "layer: W_UK absorption, decode and W_UV projection, fused against "
+                         "separate calls (dense workloads); "
                          "absorb / project: the W_UK query absorption / W_UV output projection; "
                          "prefill: non-absorbed causal MHA, B=1, T=--prefill-len, H=128")
     ap.add_argument("--prefill-len", type=int, default=4096)
@@ -382,6 +482,9 @@ def main():
         return
     if args.op == "prefill":
         bench_prefill(args)
+        return
+    if args.op == "layer":
+        bench_layer(args)
         return
 
     import mla_latent_kv_12_amd as mla

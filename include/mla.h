@@ -269,6 +269,35 @@ mla_status mla_project_out(const void *out_latent, const void *w_uv, void *o, in
                            hipStream_t stream);
 
 /*
+ * The whole absorbed decode layer for a dense (non-sparse) cache ("MLA 最佳
+ * 算子全景调研" §2: the gain of a fused decode comes from doing absorption,
+ * attention and output projection together), in four launches instead of
+ * five: the query absorption with the split-KV schedule as one more
+ * workgroup of it, the main pass, the split merge and the output
+ * projection.  Equivalent to
+ * mla_absorb_query, then mla_decode on its q_nope, then mla_project_out on
+ * the decode's out, with the same bf16 roundings of q_nope and of the
+ * latent output between the steps.
+ *   q_c, w_uk_t, w_uv, o  as mla_absorb_query / mla_project_out, with
+ *                         M = B*Sq: q_c [B, Sq, H, 128], o [B, Sq, H, 128]
+ *   q_rope, kv_pages, kv_scales, kv_dtype, num_pages, block_table,
+ *   bt_stride, cache_seqlens, softmax_scale, causal, lse
+ *                         as mla_decode (lse: natural-log lse of each row)
+ *   workspace             >= mla_layer_workspace_size(B, Sq, H, num_wg)
+ *                         bytes, 256-byte aligned; it also holds q_nope
+ *                         and the merged 512-dim rows
+ * Errors as mla_decode; nothing is enqueued on error.  Limits as mla_decode
+ * and mla_absorb_query; B*Sq*H <= 2^22.
+ */
+size_t mla_layer_workspace_size(int B, int Sq, int H, int num_wg);
+mla_status mla_decode_layer(const void *q_c, const void *w_uk_t, const void *q_rope,
+                            const void *w_uv, const void *kv_pages, const float *kv_scales,
+                            mla_kv_dtype kv_dtype, int num_pages, const int32_t *block_table,
+                            int bt_stride, const int32_t *cache_seqlens, int B, int Sq, int H,
+                            float softmax_scale, int causal, void *o, float *lse, void *workspace,
+                            size_t ws_bytes, int num_wg, hipStream_t stream);
+
+/*
  * Non-absorbed prefill: standard multi-head attention over K and V already
  * decompressed from the latent ("MLA & DSA 推理性能优化指南" §3.1: in
  * prefill c is decompressed into full K and V and a standard MHA kernel runs;

@@ -31,7 +31,8 @@ STATUS = ["MLA_OK", "MLA_ERR_NULL", "MLA_ERR_SHAPE", "MLA_ERR_UNSUPPORTED", "MLA
           "MLA_ERR_WORKSPACE", "MLA_ERR_HIP"]
 EXPORTS = ["mla_workspace_size", "mla_plan", "mla_decode", "mla_sparse_decode", "mla_attend",
            "mla_combine", "mla_kv_append", "mla_dsa_select", "mla_absorb_query", "mla_project_out",
-           "mla_prefill", "mla_decode_noalloc", "mla_status_str", "mla_last_error"]
+           "mla_prefill", "mla_decode_noalloc", "mla_layer_workspace_size", "mla_decode_layer",
+           "mla_status_str", "mla_last_error"]
 
 _lib = None
 
@@ -79,6 +80,10 @@ def lib():
                                          f32, i32, vp, vp, i32, vp]
         L.mla_prefill.restype = i32
         L.mla_prefill.argtypes = [vp, vp, vp, i32, i32, i32, f32, i32, vp, vp, vp]
+        L.mla_layer_workspace_size.restype = sz
+        L.mla_layer_workspace_size.argtypes = [i32, i32, i32, i32]
+        L.mla_decode_layer.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, vp, i32, vp, i32, i32, i32,
+                                       f32, i32, vp, vp, vp, sz, i32, vp]
         L.mla_status_str.restype = ctypes.c_char_p
         L.mla_status_str.argtypes = [i32]
         L.mla_last_error.restype = ctypes.c_char_p
@@ -320,6 +325,65 @@ def absorb_query(q_c, w_uk_t, out=None):
 def project_out(out_latent, w_uv, out=None):
     """o [..., H, 128] = W_UV . out_latent [..., H, 512] (w_uv is [H, 128, 512]) (mla_project_out)."""
     return _proj(out_latent, w_uv, 512, 128, False, out)
+
+
+def layer_workspace_size(B: int, Sq: int, H: int, num_wg: int = 0) -> int:
+    return int(lib().mla_layer_workspace_size(B, Sq, H, num_wg))
+
+
+def decode_layer(q_c, w_uk_t, q_rope, w_uv, kv_pages, block_table, cache_seqlens, softmax_scale,
+                 kv_scales=None, causal=False, o=None, lse=None, workspace=None, num_wg=0):
+    """The absorbed decode layer (mla_decode_layer): q_c [B,Sq,H,128] -> o [B,Sq,H,128]
+    through W_UK (w_uk_t [H,512,128]), the dense decode and W_UV (w_uv [H,128,512]);
+    returns (o, lse)."""
+    _req(q_c, "q_c", (torch.bfloat16,), 4)
+    B, Sq, H, dq = q_c.shape
+    if dq != 128:
+        raise ValueError("q_c must be [B,Sq,H,128]")
+    _req(w_uk_t, "w_uk_t", (torch.bfloat16,), 3)
+    _req(w_uv, "w_uv", (torch.bfloat16,), 3)
+    if tuple(w_uk_t.shape) != (H, 512, 128) or tuple(w_uv.shape) != (H, 128, 512):
+        raise ValueError("w_uk_t must be [H,512,128] and w_uv [H,128,512]")
+    dev = q_c.device
+    # argument checks of the decode part (q_nope lives in the workspace)
+    _req(q_rope, "q_rope", (torch.bfloat16,), 4)
+    if tuple(q_rope.shape) != (B, Sq, H, 64):
+        raise ValueError("q_rope must be [B,Sq,H,64]")
+    _req(kv_pages, "kv_pages", (torch.bfloat16, torch.uint8, torch.float8_e4m3fn), 3)
+    if tuple(kv_pages.shape[1:]) != (64, 576):
+        raise ValueError("kv_pages must be [num_pages, 64, 576]")
+    fp8 = kv_pages.dtype != torch.bfloat16
+    if fp8:
+        if kv_scales is None:
+            raise ValueError("an fp8 cache needs kv_scales")
+        _req(kv_scales, "kv_scales", (torch.float32,), 2)
+        if tuple(kv_scales.shape) != (kv_pages.shape[0], 64):
+            raise ValueError("kv_scales must be [num_pages, 64]")
+    _req(block_table, "block_table", (torch.int32,), 2)
+    _req(cache_seqlens, "cache_seqlens", (torch.int32,), 1)
+    if block_table.shape[0] != B or cache_seqlens.shape[0] != B:
+        raise ValueError("block_table must be [B, max_pages] and cache_seqlens [B]")
+    if o is None:
+        o = torch.empty((B, Sq, H, 128), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((B, Sq, H), dtype=torch.float32, device=dev)
+    _req(o, "o", (torch.bfloat16,), 4)
+    _req(lse, "lse", (torch.float32,), 3)
+    if tuple(o.shape) != (B, Sq, H, 128) or tuple(lse.shape) != (B, Sq, H):
+        raise ValueError("o must be [B,Sq,H,128] and lse [B,Sq,H]")
+    if workspace is None:
+        n = layer_workspace_size(B, Sq, H, num_wg)
+        if n == 0:
+            raise MLAError(2, "invalid sizes for the layer workspace")
+        workspace = torch.empty(n, dtype=torch.uint8, device=dev)
+    _req(workspace, "workspace", (torch.uint8,), 1)
+    _check(lib().mla_decode_layer(
+        q_c.data_ptr(), w_uk_t.data_ptr(), q_rope.data_ptr(), w_uv.data_ptr(), kv_pages.data_ptr(),
+        kv_scales.data_ptr() if fp8 else None, MLA_KV_FP8_E4M3 if fp8 else MLA_KV_BF16,
+        kv_pages.shape[0], block_table.data_ptr(), block_table.shape[1], cache_seqlens.data_ptr(),
+        B, Sq, H, float(softmax_scale), int(bool(causal)), o.data_ptr(), lse.data_ptr(),
+        workspace.data_ptr(), workspace.numel(), int(num_wg), _stream(q_c)))
+    return o, lse
 
 
 def prefill(q, k, v, softmax_scale, causal=True, out=None, lse=None):

@@ -130,13 +130,18 @@ mla_status fill_sched_args(const mla::Geometry& g, const int32_t* seqlens, void*
 
 // Validates a decode request and enqueues its stages (plan unless planned,
 // main pass, combine) on `stream` with the given workspace.
-mla_status mla::run_decode(const void* q_nope, const void* q_rope, const void* kv_pages,
-                           const float* kv_scales, mla_kv_dtype kv_dtype, int num_pages,
-                           const int32_t* block_table, int bt_stride, const int32_t* cache_seqlens,
-                           const int32_t* indices, int topk, int B, int Sq, int H,
-                           float softmax_scale, int causal, void* out, float* lse, void* workspace,
-                           size_t ws_bytes, int num_wg, int planned, hipStream_t stream, int stages) {
-  g_err[0] = 0;
+namespace {
+
+// Checks a decode request and folds it into its geometry and kernel
+// arguments; nothing is enqueued.
+mla_status prepare_decode(const void* q_nope, const void* q_rope, const void* kv_pages,
+                          const float* kv_scales, mla_kv_dtype kv_dtype, int num_pages,
+                          const int32_t* block_table, int bt_stride, const int32_t* cache_seqlens,
+                          const int32_t* indices, int topk, int B, int Sq, int H, float softmax_scale,
+                          int causal, void* out, float* lse, void* workspace, size_t ws_bytes,
+                          int num_wg, mla::Geometry* gp, mla::DecodeArgs* ap) {
+  mla::Geometry& g = *gp;
+  mla::DecodeArgs& a = *ap;
   if (!q_nope || !q_rope || !kv_pages || !block_table || !cache_seqlens || !out || !lse)
     return fail(MLA_ERR_NULL, "a required tensor pointer is NULL");
   if (topk > 0 && !indices) return fail(MLA_ERR_NULL, "sparse decode needs indices");
@@ -158,7 +163,6 @@ mla_status mla::run_decode(const void* q_nope, const void* q_rope, const void* k
   if (!aligned(workspace, 256)) return fail(MLA_ERR_ALIGN, "workspace must be 256-byte aligned");
   const int wg = resolve_wg(num_wg, Sq, H, topk);
   if (wg <= 0) return fail(MLA_ERR_HIP, "could not query the device's compute units");
-  mla::Geometry g;
   if (!make_geometry(B, Sq, H, topk, wg, &g)) return fail(MLA_ERR_SHAPE, "sizes out of range");
   const size_t need = mla::ws_layout(g).total;
   if (ws_bytes < need)
@@ -166,7 +170,6 @@ mla_status mla::run_decode(const void* q_nope, const void* q_rope, const void* k
   if ((long long)num_pages * mla::kPage * mla::kD * (kv_dtype == MLA_KV_BF16 ? 2 : 1) < 0)
     return fail(MLA_ERR_SHAPE, "num_pages too large");
 
-  mla::DecodeArgs a;
   memset(&a, 0, sizeof a);
   fill_sched_args(g, cache_seqlens, workspace, &a);
   a.q_nope = static_cast<const uint16_t*>(q_nope);
@@ -181,7 +184,24 @@ mla_status mla::run_decode(const void* q_nope, const void* q_rope, const void* k
   a.num_pages = num_pages;
   a.causal = (topk == 0 && causal) ? 1 : 0;
   a.scale_log2 = softmax_scale * 1.44269504088896340736f;
+  return MLA_OK;
+}
 
+}  // namespace
+
+mla_status mla::run_decode(const void* q_nope, const void* q_rope, const void* kv_pages,
+                           const float* kv_scales, mla_kv_dtype kv_dtype, int num_pages,
+                           const int32_t* block_table, int bt_stride, const int32_t* cache_seqlens,
+                           const int32_t* indices, int topk, int B, int Sq, int H,
+                           float softmax_scale, int causal, void* out, float* lse, void* workspace,
+                           size_t ws_bytes, int num_wg, int planned, hipStream_t stream, int stages) {
+  g_err[0] = 0;
+  mla::Geometry g;
+  mla::DecodeArgs a;
+  const mla_status st = prepare_decode(q_nope, q_rope, kv_pages, kv_scales, kv_dtype, num_pages, block_table,
+                                       bt_stride, cache_seqlens, indices, topk, B, Sq, H, softmax_scale, causal,
+                                       out, lse, workspace, ws_bytes, num_wg, &g, &a);
+  if (st != MLA_OK) return st;
   hipError_t e;
   const bool fp8 = kv_dtype == MLA_KV_FP8_E4M3;
   if (mla::uses_hg(g, fp8)) {
@@ -305,6 +325,86 @@ mla_status mla_combine(const int32_t* cache_seqlens, int B, int Sq, int H, int t
   a.lse = lse;
   hipError_t e = mla::launch_combine(g, a, stream);
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "combine launch: %s", hipGetErrorString(e));
+  return MLA_OK;
+}
+
+namespace {
+// Layer workspace: the decode's, then q_nope and the main pass's finished
+// rows (bf16 [B*Sq, H, 512] each).
+struct LayerLayout {
+  size_t dec, q_nope, out, total;
+};
+bool layer_layout(int B, int Sq, int H, int num_wg, LayerLayout* L, mla::Geometry* g) {
+  const int wg = resolve_wg(num_wg, Sq, H, 0);
+  if (wg <= 0 || !make_geometry(B, Sq, H, 0, wg, g)) return false;
+  auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
+  const size_t rows = (size_t)B * Sq * H;
+  L->dec = up(mla::ws_layout(*g).total);
+  L->q_nope = L->dec;
+  L->out = L->q_nope + up(rows * mla::kDC * 2);
+  L->total = L->out + up(rows * mla::kDC * 2);
+  return true;
+}
+}  // namespace
+
+size_t mla_layer_workspace_size(int B, int Sq, int H, int num_wg) {
+  if (B <= 0 || Sq <= 0 || H <= 0 || num_wg < 0 || num_wg > kMaxWg) return 0;
+  if ((long long)B * Sq * H > (1LL << 31) / 512) return 0;
+  LayerLayout L;
+  mla::Geometry g;
+  if (!layer_layout(B, Sq, H, num_wg, &L, &g)) return 0;
+  return L.total;
+}
+
+mla_status mla_decode_layer(const void* q_c, const void* w_uk_t, const void* q_rope, const void* w_uv,
+                            const void* kv_pages, const float* kv_scales, mla_kv_dtype kv_dtype,
+                            int num_pages, const int32_t* block_table, int bt_stride,
+                            const int32_t* cache_seqlens, int B, int Sq, int H, float softmax_scale,
+                            int causal, void* o, float* lse, void* workspace, size_t ws_bytes,
+                            int num_wg, hipStream_t stream) {
+  g_err[0] = 0;
+  if (!q_c || !w_uk_t || !w_uv || !o) return fail(MLA_ERR_NULL, "a required tensor pointer is NULL");
+  if (!aligned(q_c, 16) || !aligned(w_uk_t, 16) || !aligned(w_uv, 16) || !aligned(o, 16))
+    return fail(MLA_ERR_ALIGN, "q_c, w_uk_t, w_uv and o must be 16-byte aligned");
+  if (B <= 0 || Sq <= 0 || H <= 0 || H > 65535)
+    return fail(MLA_ERR_SHAPE, "need B, Sq >= 1 and 1 <= H <= 65535 (got %d, %d, %d)", B, Sq, H);
+  if ((long long)B * Sq * H > (1LL << 31) / 512) return fail(MLA_ERR_SHAPE, "B * Sq * H too large");
+  if (num_wg < 0 || num_wg > kMaxWg) return fail(MLA_ERR_SHAPE, "num_wg out of range [0, %d]", kMaxWg);
+  if (!workspace) return fail(MLA_ERR_WORKSPACE, "workspace is NULL");
+  if (!aligned(workspace, 256)) return fail(MLA_ERR_ALIGN, "workspace must be 256-byte aligned");
+  LayerLayout L;
+  mla::Geometry g0;
+  if (!layer_layout(B, Sq, H, num_wg, &L, &g0)) return fail(MLA_ERR_SHAPE, "sizes out of range");
+  if (ws_bytes < L.total)
+    return fail(MLA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, L.total);
+  uint8_t* base = static_cast<uint8_t*>(workspace);
+  mla::LayerArgs la;
+  memset(&la, 0, sizeof la);
+  mla::Geometry g;
+  const mla_status st = prepare_decode(base + L.q_nope, q_rope, kv_pages, kv_scales, kv_dtype, num_pages,
+                                       block_table, bt_stride, cache_seqlens, nullptr, 0, B, Sq, H,
+                                       softmax_scale, causal, base + L.out, lse, workspace, L.dec, num_wg,
+                                       &g, &la.d);
+  if (st != MLA_OK) return st;
+  la.pa.a = static_cast<const uint16_t*>(q_c);
+  la.pa.w = static_cast<const uint16_t*>(w_uk_t);
+  la.pa.c = reinterpret_cast<uint16_t*>(base + L.q_nope);
+  la.pa.M = B * Sq;
+  la.pa.H = H;
+  mla::ProjArgs pj;
+  pj.a = reinterpret_cast<const uint16_t*>(base + L.out);
+  pj.w = static_cast<const uint16_t*>(w_uv);
+  pj.c = static_cast<uint16_t*>(o);
+  pj.M = B * Sq;
+  pj.H = H;
+  hipError_t e = mla::launch_absorb_plan(la, stream);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "absorb launch: %s", hipGetErrorString(e));
+  e = mla::launch_decode(g, la.d, kv_dtype == MLA_KV_FP8_E4M3, stream);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+  e = mla::launch_combine(g, la.d, stream);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "combine launch: %s", hipGetErrorString(e));
+  e = mla::launch_proj(pj, false, stream);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "projection launch: %s", hipGetErrorString(e));
   return MLA_OK;
 }
 

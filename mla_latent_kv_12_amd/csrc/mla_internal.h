@@ -121,6 +121,14 @@ struct ProjArgs {
 };
 hipError_t launch_proj(const ProjArgs& a, bool absorb, hipStream_t stream);
 
+// The absorbed decode layer (mla_layer.hip): the query absorption with the
+// split-KV scheduling pass as one more workgroup of the same launch.
+struct LayerArgs {
+  DecodeArgs d;  // the decode (q_nope and out point into the workspace)
+  ProjArgs pa;   // absorption: a = q_c, w = W_UK^T, c = q_nope, M = B*Sq
+};
+hipError_t launch_absorb_plan(const LayerArgs& la, hipStream_t stream);
+
 // Non-absorbed prefill over decompressed per-head Q/K (192 dims) and V (128).
 struct PrefillArgs {
   const uint16_t* q;  // bf16 [B, T, H, 192]

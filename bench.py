@@ -85,7 +85,7 @@ def kernel_source_sha(inp=None) -> str:
     """First 16 hex of the SHA-256 of the source file holding the main
     kernel for `inp` (the head-group sparse kernel has a file of its own)."""
     name = "mla_kernels.hip"
-    if inp is not None and main_kernel_name(inp).endswith("_hg"):
+    if inp is not None and "_hg" in main_kernel_name(inp):
         name = "mla_sparse.hip"
     p = os.path.join(ROOT, "mla_latent_kv_12_amd", "csrc", name)
     return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
@@ -158,7 +158,9 @@ def settle(fn, seconds: float):
 def main_kernel_name(inp) -> str:
     """Name of the main-pass kernel the library launches for this input."""
     if inp["indices"] is not None and inp["kv_dtype"] != "fp8":
-        return "decode_bf16_sparse_hg"   # head-group kernel: the whole sparse step
+        # head-group kernel, then the merge of split index ranges: the
+        # attend stage (and the whole sparse step)
+        return "decode_bf16_sparse_hg + combine_hg"
     rows = inp["H"] if inp["indices"] is not None else inp["Sq"] * inp["H"]
     rows = min(rows, 128)
     shape = "r4" if rows > 64 else "r2" if rows > 32 else "r1w"

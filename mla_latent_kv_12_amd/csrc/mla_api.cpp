@@ -108,6 +108,7 @@ mla_status fill_sched_args(const mla::Geometry& g, const int32_t* seqlens, void*
   a->ws_cost = reinterpret_cast<int32_t*>(base + w.cost);
   a->ws_meta = reinterpret_cast<int32_t*>(base + w.meta);
   a->ws_plse = reinterpret_cast<float*>(base + w.plse);
+  a->ws_psc = reinterpret_cast<float*>(base + w.psc);
   a->ws_po = reinterpret_cast<float*>(base + w.po);
   a->ws_zero = base + w.zero;
   a->B = g.B;

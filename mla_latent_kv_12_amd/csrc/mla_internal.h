@@ -57,7 +57,9 @@ struct WsLayout {
   size_t cost;   // int32 [n_units + 1]        prefix of per-unit cost
   size_t meta;   // int32 [n_units * 4]        n_tiles, split_base, n_splits, g_first
   size_t plse;   // f32   [max_splits * split_rows]   partial log2-sum-exp
-  size_t po;     // f32   [max_splits * split_rows * 512] partial normalised outputs
+  size_t psc;    // f32   [max_splits * split_rows]   partial row scale (largest |O/l|)
+  size_t po;     // f16   [max_splits * split_rows * 512] partial O/l divided by the row scale
+                 // (the head-group sparse kernel: f32 O/l, 32-row ranges)
   size_t zero;   // 1280 zero bytes: copy source for cache rows that are not visible
   size_t total;
 };
@@ -78,6 +80,7 @@ struct DecodeArgs {
   int32_t* ws_cost;
   int32_t* ws_meta;
   float* ws_plse;
+  float* ws_psc;
   float* ws_po;
   const uint8_t* ws_zero;
   int bt_stride;

@@ -709,22 +709,59 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
           }
         }
         if (lse_writer) a.lse[(size_t)ui.row0 + r] = empty ? kNegInf : lse2 * kLn2;
-      } else {
-        // Partials are stored in fragment order (see combine_kernel): each
-        // store writes 1 KB of consecutive bytes, one 16-byte piece per lane.
-        float* dst = a.ws_po + (size_t)split * (32 * R * kDC) + 4 * ln;
+      }
+    }
+    if (n_splits <= 1) return;
+    // A split unit stores its normalised partial O/l as fp16 of O/(l M),
+    // M = the row's largest |O/l| over all 512 dims (kept in fp32 beside the
+    // log2 lse): the values lie in [-1, 1], so fp16 has the range, and its
+    // rounding error is at most 2^-11 M, a quarter of the output's own bf16
+    // rounding, for half the bytes written and read back.  The row maximum
+    // is taken over the waves (each holds 512/R of the dims) through the P
+    // buffers, which no wave reads any more (the barrier above).
+    float* const rmax = reinterpret_cast<float*>(lds + W::kPOff);
 #pragma unroll
-        for (int dbl = 0; dbl < DB; dbl++) {
-          const int db = DB * rg + dbl;
-          const f32x16& ob = o[dbl * R + rb];
+    for (int rb = 0; rb < R; rb++) {
+      const int r = 32 * rb + l32;
+      float mx = 0.f;
 #pragma unroll
-          for (int q = 0; q < 4; q++) {
-            f32x4 w = {acc_get(ob, 4 * q) * inv, acc_get(ob, 4 * q + 1) * inv,
-                       acc_get(ob, 4 * q + 2) * inv, acc_get(ob, 4 * q + 3) * inv};
-            *reinterpret_cast<f32x4*>(dst + 256 * ((rb * 16 + db) * 4 + q)) = w;
-          }
+      for (int dbl = 0; dbl < DB; dbl++)
+#pragma unroll
+        for (int i = 0; i < 16; i++) mx = fmaxf(mx, fabsf(acc_get(o[dbl * R + rb], i)));
+      mx = pair_max(mx);
+      if (g == 0) rmax[R * r + rg] = mx;
+    }
+    wait_lds();
+    barrier();
+    _Float16* const dst = reinterpret_cast<_Float16*>(a.ws_po) + (size_t)split * (32 * R * kDC) + 4 * ln;
+#pragma unroll
+    for (int rb = 0; rb < R; rb++) {
+      const int r = 32 * rb + l32;
+      if (r >= ui.rows) continue;
+      const float lf = ll[r];
+      const bool empty = !(lf > 0.f);
+      const float inv = empty ? 0.f : 1.0f / lf;
+      float mxo = 0.f;
+#pragma unroll
+      for (int k = 0; k < R; k++) mxo = fmaxf(mxo, rmax[R * r + k]);
+      const float scale = mxo * inv;                 // the row's largest |O/l|
+      const float f = scale > 0.f ? inv / scale : 0.f;
+      // fragment order (see combine_kernel): each store writes 512
+      // consecutive bytes, 8 per lane
+#pragma unroll
+      for (int dbl = 0; dbl < DB; dbl++) {
+        const int db = DB * rg + dbl;
+        const f32x16& ob = o[dbl * R + rb];
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+          f16x4 w = {(_Float16)(acc_get(ob, 4 * q) * f), (_Float16)(acc_get(ob, 4 * q + 1) * f),
+                     (_Float16)(acc_get(ob, 4 * q + 2) * f), (_Float16)(acc_get(ob, 4 * q + 3) * f)};
+          *reinterpret_cast<f16x4*>(dst + 256 * ((rb * 16 + db) * 4 + q)) = w;
         }
-        if (lse_writer) a.ws_plse[(size_t)split * (32 * R) + r] = lse2;
+      }
+      if (g == 0 && rg == 0) {
+        a.ws_plse[(size_t)split * (32 * R) + r] = empty ? kNegInf : mm[r] + __log2f(lf);
+        a.ws_psc[(size_t)split * (32 * R) + r] = scale;
       }
     }
   };
@@ -902,11 +939,13 @@ MLA_WIDE_KERNEL(decode_fp8_sparse_r2, true, true, 2)
 // results; units with no tokens at all get out = 0, lse = -inf.
 //
 // Partial layout per split (32 * R rows, R the waves of the kernel shape):
-// 64 * R blocks of 1 KB in fragment order.  Block
-// (rb, db, q) = (rb * 16 + db) * 4 + q holds, at lane L = 32 g + l (16 bytes
-// each), row 32 rb + l, dims 32 db + 8 q + 4 g .. +3: the order in which a
-// wave's accumulators leave the registers.  Each 64-thread group of a block
-// merges one fragment block: thread L handles row 32 rb + l, 4 dims.
+// 64 * R blocks of 512 bytes in fragment order.  Block
+// (rb, db, q) = (rb * 16 + db) * 4 + q holds, at lane L = 32 g + l (four
+// fp16, 8 bytes), row 32 rb + l, dims 32 db + 8 q + 4 g .. +3, divided by the
+// row's scale: the order in which a wave's accumulators leave the registers.
+// Per split and row: the log2 lse and the scale (fp32).  Each 64-thread
+// group of a block merges one fragment block: thread L handles row
+// 32 rb + l, 4 dims.
 // ---------------------------------------------------------------------------
 template <bool SPARSE>
 __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
@@ -927,6 +966,12 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   // a time so that several loads are in flight per thread.
   const int base = a.ws_meta[4 * uu + 1];
   const size_t frag = (size_t)blk * 256 + 4 * ln;
+  const _Float16* const po = reinterpret_cast<const _Float16*>(a.ws_po);
+  auto piece = [&](size_t sp) -> f32x4 {
+    const f16x4 h = *reinterpret_cast<const f16x4*>(po + sp * ((size_t)a.split_rows * kDC) + frag);
+    const float sc = a.ws_psc[sp * a.split_rows + r];
+    return f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]} * sc;
+  };
   float mx = kNegInf, wsum = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   auto merge = [&](float li, const f32x4& v) {
@@ -946,15 +991,14 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
     for (int j = 0; j < 4; j++) {
       const size_t sp = (size_t)(base + i + j);
       l4[j] = a.ws_plse[sp * a.split_rows + r];
-      v4[j] = *reinterpret_cast<const f32x4*>(a.ws_po + sp * ((size_t)a.split_rows * kDC) + frag);
+      v4[j] = piece(sp);
     }
 #pragma unroll
     for (int j = 0; j < 4; j++) merge(l4[j], v4[j]);
   }
   for (; i < ns; i++) {
     const size_t sp = (size_t)(base + i);
-    merge(a.ws_plse[sp * a.split_rows + r],
-          *reinterpret_cast<const f32x4*>(a.ws_po + sp * ((size_t)a.split_rows * kDC) + frag));
+    merge(a.ws_plse[sp * a.split_rows + r], piece(sp));
   }
   if (ns == 0 || mx == kNegInf) {
     *reinterpret_cast<u32x2*>(dst) = u32x2{0u, 0u};
@@ -1016,17 +1060,22 @@ WsLayout ws_layout(const Geometry& g) {
   off = up(off + sizeof(int32_t) * (size_t)(g.n_units + 1));
   w.meta = off;
   off = up(off + sizeof(int32_t) * 4 * (size_t)g.n_units);
-  // partials: split units of the persistent kernels, or the ranges of the
-  // head-group sparse decode (32 rows each), whichever needs more
+  // partials: split units of the persistent kernels (fp16 values, fp32 lse
+  // and scale per row), or the ranges of the head-group sparse decode (32
+  // rows each, fp32 values and lse), whichever needs more
   size_t part_rows = (size_t)g.max_splits * g.split_rows;
+  size_t po_bytes = sizeof(uint16_t) * part_rows * kDC;
   if (g.sparse && g.hg_splits > 1) {
     const size_t hg_rows = (size_t)g.n_su * g.hg_groups * g.hg_splits * 32;
     if (hg_rows > part_rows) part_rows = hg_rows;
+    if (sizeof(float) * hg_rows * kDC > po_bytes) po_bytes = sizeof(float) * hg_rows * kDC;
   }
   w.plse = off;
   off = up(off + sizeof(float) * part_rows);
+  w.psc = off;
+  off = up(off + sizeof(float) * part_rows);
   w.po = off;
-  off = up(off + sizeof(float) * part_rows * kDC);
+  off = up(off + po_bytes);
   w.zero = off;
   off = up(off + 1280);
   w.total = off;

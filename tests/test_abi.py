@@ -46,8 +46,9 @@ def test_workspace_size_rules():
     assert ws(64, 1, 128, 0, -1) == 0
     a = ws(64, 1, 128, 0, 256)
     assert a > 0 and a % 256 == 0
-    # partial buffers: (num_wg + units) * 128 rows * (512 + 1) floats at least
-    assert a >= (256 + 64) * 128 * 513 * 4
+    # partial buffers: (num_wg + units) * 128 rows * (512 fp16 values + fp32
+    # lse and scale) at least
+    assert a >= (256 + 64) * 128 * (512 * 2 + 8)
     assert ws(64, 1, 128, 0, 512) > a          # more workgroups, more splits
     assert ws(4, 2, 128, 0, 256) > ws(4, 1, 128, 0, 256)  # 256 rows -> 2 units per sequence
     assert ws(32, 1, 128, 1024, 256) > 0       # sparse

@@ -110,7 +110,6 @@ mla_status fill_sched_args(const mla::Geometry& g, const int32_t* seqlens, void*
   a->ws_plse = reinterpret_cast<float*>(base + w.plse);
   a->ws_psc = reinterpret_cast<float*>(base + w.psc);
   a->ws_po = reinterpret_cast<float*>(base + w.po);
-  a->ws_zero = base + w.zero;
   a->B = g.B;
   a->Sq = g.Sq;
   a->H = g.H;
@@ -214,8 +213,13 @@ mla_status mla::run_decode(const void* q_nope, const void* q_rope, const void* k
     return MLA_OK;
   }
   if ((stages & mla::kStagePlan) && !planned) {
-    e = mla::launch_plan(g, a, stream);
-    if (e != hipSuccess) return fail(MLA_ERR_HIP, "plan launch: %s", hipGetErrorString(e));
+    if (g.n_units <= mla::kFoldUnits) {
+      // the main pass schedules itself: one launch less
+      a.fold_plan = 1;
+    } else {
+      e = mla::launch_plan(g, a, stream);
+      if (e != hipSuccess) return fail(MLA_ERR_HIP, "plan launch: %s", hipGetErrorString(e));
+    }
   }
   if (stages & mla::kStageAttend) {
     e = mla::launch_decode(g, a, fp8, stream);

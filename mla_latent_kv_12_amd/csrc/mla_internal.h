@@ -26,6 +26,9 @@ constexpr int kTileFp8 = kPage * kBytesFp8Row;    // 36864
 // never given less work.
 constexpr int kSplitCost = 6;
 constexpr int kMinWgCost = 2;
+// Decodes of up to this many units schedule themselves inside the main pass
+// (its LDS holds the cost prefix); larger ones get a scheduling launch.
+constexpr int kFoldUnits = 2048;
 
 // Problem geometry after the host has folded (B, Sq, H, sparse) into units.
 // A "sequence unit" (su) is a set of query rows that attend over the same
@@ -60,7 +63,6 @@ struct WsLayout {
   size_t psc;    // f32   [max_splits * split_rows]   partial row scale (largest |O/l|)
   size_t po;     // f16   [max_splits * split_rows * 512] partial O/l divided by the row scale
                  // (the head-group sparse kernel: f32 O/l, 32-row ranges)
-  size_t zero;   // 1280 zero bytes: copy source for cache rows that are not visible
   size_t total;
 };
 
@@ -82,7 +84,6 @@ struct DecodeArgs {
   float* ws_plse;
   float* ws_psc;
   float* ws_po;
-  const uint8_t* ws_zero;
   int bt_stride;
   int num_pages;
   int B, Sq, H, topk;
@@ -90,6 +91,7 @@ struct DecodeArgs {
   int causal;
   float scale_log2;  // softmax_scale * log2(e)
   int hg_groups, hg_splits, hg_span;
+  int fold_plan;  // the main pass computes its own schedule (no scheduling launch)
 };
 
 // Cache append: the Sq new latent rows of every sequence into their slots.

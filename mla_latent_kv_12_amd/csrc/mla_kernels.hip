@@ -35,6 +35,10 @@ __global__ __launch_bounds__(256) void plan_kernel(DecodeArgs a) {
   plan_work<SPARSE>(a);
 }
 
+// Copy source for cache rows that are not visible: zeros (their weights are
+// 0, and the values they contribute must be finite).
+__device__ __attribute__((aligned(256))) const uint8_t kZeroSrc[1280] = {};
+
 // bf16 region-A swizzle of a cached row: the 16-byte chunk c of row r sits at
 // position c ^ sw16(r).  The score operand reads one chunk of 16 consecutive
 // rows per 16 lanes (sw16 is a bijection on r & 15) and the transposed value
@@ -114,6 +118,8 @@ struct Wide {
   static constexpr int kDummyOff = kMrgOff + 2 * 32 * R * 4;
   static constexpr int kLdsBytes = kDummyOff + 64;
   static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+  static_assert(4 * (2 * (kFoldUnits + 1) + kThreads) <= kSlots * kABlk,
+                "the self-schedule's scratch fits in the chunk ring");
   static_assert(kABlk % 1024 == 0 && kBBlk % 16 == 0 && kBOff % 16 == 0, "block alignment");
   // vector-memory operations wave w issues per step: its copies, plus the
   // lookups of wave 0
@@ -157,15 +163,30 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
   // The lookup cursor walks the workgroup's chunks: unit cu (-1 once done),
   // tile ct, half ch, tile range end chi, sequence (dense b / sparse su) cs
   // and its length cL.  Every wave runs it (uniform scalar code).
-  const int u_end = ldc(a.ws_work + 2 * wg + 2), t_end = ldc(a.ws_work + 2 * wg + 3);
-  int cu = ldc(a.ws_work + 2 * wg), ct = ldc(a.ws_work + 2 * wg + 1), ch = 0, chi = 0, cs = 0, cL = 0;
+  // This workgroup's share of the schedule: computed here (the LDS ring is
+  // still free) unless a scheduling launch already wrote it.
+  WgSched sc;
+  if (a.fold_plan) {
+    sc = sched_in_wg<SPARSE>(a, reinterpret_cast<int*>(lds), W::kThreads, tid, wg);
+  } else {
+    sc.u0 = ldc(a.ws_work + 2 * wg);
+    sc.t0 = ldc(a.ws_work + 2 * wg + 1);
+    sc.u1 = ldc(a.ws_work + 2 * wg + 2);
+    sc.t1 = ldc(a.ws_work + 2 * wg + 3);
+    sc.q = max((ldc(a.ws_cost + a.n_units) + a.num_wg - 1) / a.num_wg, kMinWgCost);
+    const int uc = min(sc.u0, a.n_units - 1);
+    sc.c0 = ldc(a.ws_cost + uc);
+    sc.b0 = ldc(a.ws_meta + 4 * uc + 1);
+  }
+  const int u_end = sc.u1, t_end = sc.t1;
+  int cu = sc.u0, ct = sc.t0, ch = 0, chi = 0, cs = 0, cL = 0;
   auto enter = [&]() {  // settle (cu, ct) on the next unit with a chunk left
     for (;;) {
       if (cu > u_end || cu >= a.n_units) {
         cu = -1;
         return;
       }
-      chi = (cu == u_end) ? t_end : ldc(a.ws_meta + 4 * cu);
+      chi = (cu == u_end) ? t_end : unit_tiles(a, SPARSE, cu);
       if (ct < chi) break;
       cu++;
       ct = 0;
@@ -266,7 +287,7 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
   };
   // Where item z's rows come from (read from its descriptor and rings).
   auto source_dense = [&](const DD& d) -> Src {
-    Src r{a.ws_zero, reinterpret_cast<const float*>(a.ws_zero), 0, -1, {}};
+    Src r{kZeroSrc, reinterpret_cast<const float*>(kZeroSrc), 0, -1, {}};
     r.nvalid = dd_nvalid(d);
     if (r.nvalid > 0) {
       const int half = d.remh & 1;
@@ -277,7 +298,7 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
     return r;
   };
   auto source = [&](int z, const Desc& dz) -> Src {
-    Src r{a.ws_zero, reinterpret_cast<const float*>(a.ws_zero), 0, -1, {}};
+    Src r{kZeroSrc, reinterpret_cast<const float*>(kZeroSrc), 0, -1, {}};
     const int uu = dz.u, th = dz.th, LL = dz.L;
     {
       int ln = lane;
@@ -299,7 +320,7 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
   auto copy = [&](int j, uint32_t slot, uint32_t slotb, const Src& sr) {
     int ln = lane;
     asm volatile("" : "+v"(ln));  // keeps per-lane offsets from being hoisted out of the loop
-    const uint8_t* zero = a.ws_zero;
+    const uint8_t* zero = kZeroSrc;
     auto rowsrc = [&](int row, uint32_t off) -> const uint8_t* {  // per-lane row
       if constexpr (!SPARSE) return row < sr.nvalid ? sr.base + row * W::kRowBytes + off : zero + off;
       else {
@@ -663,6 +684,9 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
   // ------------------------------------------------------------ epilogue
   // Normalises this wave's dims of every row and writes them to out/lse
   // (unit finished here) or to the unit's split partials.
+  // The epilogue's unit eu with its cost prefix and split-index prefix,
+  // walked forward as segments end (units are finished in order).
+  int eu = sc.u0, eC = sc.c0, eB = sc.b0;
   auto end_segment = [&](const UnitInfo& ui, int uu) {
     // Lane-derived offsets are recomputed here rather than kept live (and
     // spilled) across the whole loop; a spill reload would wait for every
@@ -683,8 +707,16 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
     }
     wait_lds();
     barrier();
-    const int n_splits = a.ws_meta[4 * uu + 2];
-    const int split = a.ws_meta[4 * uu + 1] + (wg - a.ws_meta[4 * uu + 3]);
+    for (; eu < uu; eu++) {
+      const int n = unit_tiles(a, SPARSE, eu);
+      int ns, gf;
+      unit_splits(eC, n, sc.q, &ns, &gf);
+      eC += n + kSplitCost;
+      eB += ns;
+    }
+    int n_splits, gfirst;
+    unit_splits(eC, unit_tiles(a, SPARSE, uu), sc.q, &n_splits, &gfirst);
+    const int split = eB + (wg - gfirst);
 #pragma unroll
     for (int rb = 0; rb < R; rb++) {
       const int r = 32 * rb + l32;
@@ -1076,8 +1108,6 @@ WsLayout ws_layout(const Geometry& g) {
   off = up(off + sizeof(float) * part_rows);
   w.po = off;
   off = up(off + po_bytes);
-  w.zero = off;
-  off = up(off + 1280);
   w.total = off;
   return w;
 }

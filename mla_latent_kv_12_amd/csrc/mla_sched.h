@@ -77,9 +77,6 @@ __device__ __forceinline__ void plan_work(const DecodeArgs& a) {
     C[U] = total;
     if (in_lds) c_lds[U] = total;
   }
-  // the zero row the main kernel copies in place of invisible cache rows
-  if (tid < 1280 / 16) reinterpret_cast<i32x4*>(const_cast<uint8_t*>(a.ws_zero))[tid] = i32x4{0, 0, 0, 0};
-  __threadfence_block();
   __syncthreads();
 
   const int Q = max((total + G - 1) / G, kMinWgCost);
@@ -139,6 +136,121 @@ __device__ __forceinline__ void plan_work(const DecodeArgs& a) {
     a.ws_meta[4 * u + 3] = gf;
     base += ns;
   }
+}
+
+// What one workgroup of the main pass needs of the schedule: its first and
+// last (unit, tile) -- [u0, t0) up to (u1, t1), tiles of u1 below t1 -- the
+// cost quantum q, and the cost prefix c0 and split-index prefix b0 at its
+// first unit; later units' values follow from these by walking the units in
+// order (split_of).
+struct WgSched {
+  int u0, t0, u1, t1, q, c0, b0;
+};
+
+// Splits of a unit of n tiles whose cost interval starts at c, and the
+// first workgroup that holds one (-1 for a unit with no tile).
+__device__ __forceinline__ void unit_splits(int c, int n, int q, int* ns, int* gf) {
+  if (n <= 0) {
+    *ns = 0;
+    *gf = -1;
+    return;
+  }
+  *gf = (c + kSplitCost) / q;
+  *ns = (c + kSplitCost + n - 1) / q - *gf + 1;
+}
+
+// Units the main pass schedules for itself (up to kFoldUnits), in the LDS
+// it has not started using yet (2 (U + 1) + nthr ints), instead of reading
+// a separate scheduling launch's output: every workgroup computes the same
+// cost prefix and finds its own share, and the workgroup whose share holds
+// a unit's cost position writes that unit's metadata for the split merge.
+
+template <bool SPARSE>
+__device__ WgSched sched_in_wg(const DecodeArgs& a, int* scr, int nthr, int tid, int wg) {
+  const int U = a.n_units, G = a.num_wg;
+  int* const C = scr;           // [U + 1] cost prefix
+  int* const NS = C + U + 1;    // [U + 1] prefix of split counts
+  int* const part = NS + U + 1; // [nthr]
+  const int per = (U + nthr - 1) / nthr;
+  const int lo = min(U, tid * per), hi = min(U, lo + per);
+  auto scan = [&](int v) -> int {  // inclusive prefix of v over the threads
+    part[tid] = v;
+    __syncthreads();
+    for (int off = 1; off < nthr; off <<= 1) {
+      const int w = tid >= off ? part[tid - off] : 0;
+      __syncthreads();
+      part[tid] += w;
+      __syncthreads();
+    }
+    const int r = part[tid];
+    __syncthreads();
+    return r;
+  };
+  int s = 0;
+  for (int u = lo; u < hi; u++) s += unit_tiles(a, SPARSE, u) + kSplitCost;
+  const int incl = scan(s);
+  int run = incl - s;
+  for (int u = lo; u < hi; u++) {
+    C[u] = run;
+    run += unit_tiles(a, SPARSE, u) + kSplitCost;
+  }
+  if (tid == nthr - 1) C[U] = incl;
+  __syncthreads();
+  const int total = C[U];
+  const int q = max((total + G - 1) / G, kMinWgCost);
+  int ns_sum = 0;
+  for (int u = lo; u < hi; u++) {
+    int ns, gf;
+    unit_splits(C[u], C[u + 1] - C[u] - kSplitCost, q, &ns, &gf);
+    ns_sum += ns;
+  }
+  const int ns_incl = scan(ns_sum);
+  int base = ns_incl - ns_sum;
+  for (int u = lo; u < hi; u++) {
+    const int n = C[u + 1] - C[u] - kSplitCost;
+    int ns, gf;
+    unit_splits(C[u], n, q, &ns, &gf);
+    NS[u] = base;
+    if (C[u] / q == wg) {  // one writer per unit
+      a.ws_meta[4 * u + 0] = n;
+      a.ws_meta[4 * u + 1] = base;
+      a.ws_meta[4 * u + 2] = ns;
+      a.ws_meta[4 * u + 3] = gf;
+    }
+    base += ns;
+  }
+  if (tid == nthr - 1) NS[U] = ns_incl;
+  __syncthreads();
+  // this workgroup's share [wg q, (wg + 1) q) of the cost line
+  auto locate = [&](long long x, int* u, int* t) {
+    if (x >= total) {
+      *u = U;
+      *t = 0;
+      return;
+    }
+    int l = 0, h = U;  // C[l] <= x < C[h]
+    while (h - l > 1) {
+      const int mid = (l + h) >> 1;
+      if (C[mid] <= x) l = mid; else h = mid;
+    }
+    *u = l;
+    *t = max(0, (int)(x - C[l]) - kSplitCost);
+  };
+  WgSched w;
+  locate((long long)wg * q, &w.u0, &w.t0);
+  locate((long long)(wg + 1) * q, &w.u1, &w.t1);
+  w.q = q;
+  w.c0 = C[min(w.u0, U)];
+  w.b0 = NS[min(w.u0, U)];
+  w.u0 = __builtin_amdgcn_readfirstlane(w.u0);
+  w.t0 = __builtin_amdgcn_readfirstlane(w.t0);
+  w.u1 = __builtin_amdgcn_readfirstlane(w.u1);
+  w.t1 = __builtin_amdgcn_readfirstlane(w.t1);
+  w.q = __builtin_amdgcn_readfirstlane(w.q);
+  w.c0 = __builtin_amdgcn_readfirstlane(w.c0);
+  w.b0 = __builtin_amdgcn_readfirstlane(w.b0);
+  __syncthreads();  // the scratch is the LDS ring: free it for the copies
+  return w;
 }
 
 }  // namespace kern

@@ -587,6 +587,7 @@ def main():
     t_end.record()
     torch.cuda.synchronize()
     ms = t_start.elapsed_time(t_end) / (n_rep * args.copies)
+    settle(g_step, args.settle_s / 2)
     ms_one_per_graph = timed(g_step)
     assert torch.isfinite(lse).all(), "non-finite lse"
     # the same step as plain stream launches from Python (one mla_decode call
@@ -594,6 +595,10 @@ def main():
     for k in range(args.warmup):
         step(k)
     ms_eager = timed(step)
+    # every graph timed below first runs on its own until the clocks settle:
+    # the host-side work in between leaves the GPU idle long enough to drop
+    # them again (a main kernel timed right after it ran ~15% slower)
+    settle(g_planned, args.settle_s / 2)
     ms_planned = timed(g_planned)
 
     # The main kernel on its own: one graph holding 4 * copies back-to-back
@@ -606,9 +611,8 @@ def main():
     with torch.cuda.graph(many):
         for j in range(per):
             attend(j)
-    reps = max(1, args.steps // per)
-    for k in range(2):
-        many.replay()
+    reps = max(3, args.steps // per)
+    settle(lambda k: many.replay(), args.settle_s)
     torch.cuda.synchronize()
     t_start.record()
     for k in range(reps):
@@ -618,6 +622,7 @@ def main():
     attend_ms = t_start.elapsed_time(t_end) / (reps * per)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
+    settle(g_attend, args.settle_s / 2)
     for k in range(args.steps):
         evs[k][0].record()
         g_attend(k)

@@ -13,6 +13,7 @@ SOURCES = [os.path.join(CSRC, "mla_kernels.hip"), os.path.join(CSRC, "mla_cache.
            os.path.join(CSRC, "mla_select.hip"), os.path.join(CSRC, "mla_proj.hip"),
            os.path.join(CSRC, "mla_prefill.hip"), os.path.join(CSRC, "mla_noalloc.hip"),
            os.path.join(CSRC, "mla_sparse.hip"), os.path.join(CSRC, "mla_layer.hip"),
+           os.path.join(CSRC, "mla_combine.hip"),
            os.path.join(CSRC, "mla_api.cpp")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

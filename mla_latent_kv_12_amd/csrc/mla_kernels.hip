@@ -17,7 +17,7 @@
 //                   bf16 MFMA 32x32x16 with fp32 accumulation, online softmax
 //                   in the log2 domain; fp8 e4m3 chunks are converted to bf16
 //                   in registers (exact)
-//   combine_kernel  log-sum-exp merge of the partial results of split units
+// (the log-sum-exp merge of split units' partial results is in mla_combine.hip)
 //
 // Wave roles: the R waves of a workgroup (R = 4, 2, 1 for units of up to
 // 128, 64, 32 query rows) share each chunk in LDS.  For the scores a wave
@@ -778,7 +778,7 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
       for (int k = 0; k < R; k++) mxo = fmaxf(mxo, rmax[R * r + k]);
       const float scale = mxo * inv;                 // the row's largest |O/l|
       const float f = scale > 0.f ? inv / scale : 0.f;
-      // fragment order (see combine_kernel): each store writes 512
+      // fragment order (see the split merge in mla_combine.hip): each store writes 512
       // consecutive bytes, 8 per lane
 #pragma unroll
       for (int dbl = 0; dbl < DB; dbl++) {
@@ -966,84 +966,6 @@ MLA_WIDE_KERNEL(decode_fp8_sparse_r4, true, true, 4)
 MLA_WIDE_KERNEL(decode_fp8_sparse_r2, true, true, 2)
 #undef MLA_WIDE_KERNEL
 
-// ---------------------------------------------------------------------------
-// Combine: for units with >= 2 splits merge the partial (O/l, log2 lse)
-// results; units with no tokens at all get out = 0, lse = -inf.
-//
-// Partial layout per split (32 * R rows, R the waves of the kernel shape):
-// 64 * R blocks of 512 bytes in fragment order.  Block
-// (rb, db, q) = (rb * 16 + db) * 4 + q holds, at lane L = 32 g + l (four
-// fp16, 8 bytes), row 32 rb + l, dims 32 db + 8 q + 4 g .. +3, divided by the
-// row's scale: the order in which a wave's accumulators leave the registers.
-// Per split and row: the log2 lse and the scale (fp32).  Each 64-thread
-// group of a block merges one fragment block: thread L handles row
-// 32 rb + l, 4 dims.
-// ---------------------------------------------------------------------------
-template <bool SPARSE>
-__global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
-  const int uu = blockIdx.x;
-  const int ns = a.ws_meta[4 * uu + 2];
-  if (ns == 1) return;
-  const int blk = blockIdx.y * 4 + (threadIdx.x >> 6);
-  const int ln = threadIdx.x & 63;
-  const int q = blk & 3, db = (blk >> 2) & 15, rb = blk >> 6;
-  const int r = 32 * rb + (ln & 31);
-  UnitInfo ui = unit_info(a, SPARSE, uu);
-  if (r >= ui.rows) return;
-  const int d4 = 32 * db + 8 * q + 4 * (ln >> 5);
-  const size_t grow = (size_t)ui.row0 + r;
-  uint16_t* dst = a.out + grow * kDC + d4;
-  const bool lse_writer = db == 0 && q == 0 && ln < 32;
-  // One pass with a running maximum; the partials are loaded four splits at
-  // a time so that several loads are in flight per thread.
-  const int base = a.ws_meta[4 * uu + 1];
-  const size_t frag = (size_t)blk * 256 + 4 * ln;
-  const _Float16* const po = reinterpret_cast<const _Float16*>(a.ws_po);
-  auto piece = [&](size_t sp) -> f32x4 {
-    const f16x4 h = *reinterpret_cast<const f16x4*>(po + sp * ((size_t)a.split_rows * kDC) + frag);
-    const float sc = a.ws_psc[sp * a.split_rows + r];
-    return f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]} * sc;
-  };
-  float mx = kNegInf, wsum = 0.f;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  auto merge = [&](float li, const f32x4& v) {
-    const float mn = fmaxf(mx, li);
-    if (mn == kNegInf) return;  // nothing seen yet
-    const float sc = __builtin_amdgcn_exp2f(mx - mn);  // 0 while mx is -inf
-    const float w = __builtin_amdgcn_exp2f(li - mn);   // 0 for an empty split
-    acc = acc * sc + w * v;
-    wsum = wsum * sc + w;
-    mx = mn;
-  };
-  int i = 0;
-  for (; i + 4 <= ns; i += 4) {
-    float l4[4];
-    f32x4 v4[4];
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const size_t sp = (size_t)(base + i + j);
-      l4[j] = a.ws_plse[sp * a.split_rows + r];
-      v4[j] = piece(sp);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; j++) merge(l4[j], v4[j]);
-  }
-  for (; i < ns; i++) {
-    const size_t sp = (size_t)(base + i);
-    merge(a.ws_plse[sp * a.split_rows + r], piece(sp));
-  }
-  if (ns == 0 || mx == kNegInf) {
-    *reinterpret_cast<u32x2*>(dst) = u32x2{0u, 0u};
-    if (lse_writer) a.lse[grow] = kNegInf;
-    return;
-  }
-  const float inv = 1.0f / wsum;
-  bf16x2 p0 = {(__bf16)(acc[0] * inv), (__bf16)(acc[1] * inv)};
-  bf16x2 p1 = {(__bf16)(acc[2] * inv), (__bf16)(acc[3] * inv)};
-  *reinterpret_cast<u32x2*>(dst) = u32x2{__builtin_bit_cast(unsigned, p0), __builtin_bit_cast(unsigned, p1)};
-  if (lse_writer) a.lse[grow] = (mx + __log2f(wsum)) * kLn2;
-}
-
 template <bool FP8, bool SPARSE, int R>
 hipError_t launch_wide(void (*kern)(DecodeArgs), const Geometry& g, const DecodeArgs& a,
                        hipStream_t stream) {
@@ -1122,15 +1044,6 @@ hipError_t launch_plan(const Geometry& g, const DecodeArgs& a, hipStream_t strea
 
 hipError_t launch_decode(const Geometry& g, const DecodeArgs& a, bool fp8, hipStream_t stream) {
   return launch_variant(fp8, g.sparse != 0, g, a, stream);
-}
-
-hipError_t launch_combine(const Geometry& g, const DecodeArgs& a, hipStream_t stream) {
-  dim3 grid(g.n_units, ((g.m_unit + 31) / 32) * 16);  // 4 fragment blocks of 1 KB per block
-  if (g.sparse)
-    hipLaunchKernelGGL(combine_kernel<true>, grid, dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL(combine_kernel<false>, grid, dim3(256), 0, stream, a);
-  return hipGetLastError();
 }
 
 }  // namespace mla

@@ -1016,18 +1016,20 @@ WsLayout ws_layout(const Geometry& g) {
   off = up(off + sizeof(int32_t) * 4 * (size_t)g.n_units);
   // partials: split units of the persistent kernels (fp16 values, fp32 lse
   // and scale per row), or the ranges of the head-group sparse decode (32
-  // rows each, fp32 values and lse), whichever needs more
+  // rows each, fp16 values, fp32 lse per row and scale per row and quarter
+  // of the dims), whichever needs more
   size_t part_rows = (size_t)g.max_splits * g.split_rows;
-  size_t po_bytes = sizeof(uint16_t) * part_rows * kDC;
+  size_t sc_count = part_rows;
   if (g.sparse && g.hg_splits > 1) {
     const size_t hg_rows = (size_t)g.n_su * g.hg_groups * g.hg_splits * 32;
     if (hg_rows > part_rows) part_rows = hg_rows;
-    if (sizeof(float) * hg_rows * kDC > po_bytes) po_bytes = sizeof(float) * hg_rows * kDC;
+    if (4 * hg_rows > sc_count) sc_count = 4 * hg_rows;
   }
+  const size_t po_bytes = sizeof(uint16_t) * part_rows * kDC;
   w.plse = off;
   off = up(off + sizeof(float) * part_rows);
   w.psc = off;
-  off = up(off + sizeof(float) * part_rows);
+  off = up(off + sizeof(float) * sc_count);
   w.po = off;
   off = up(off + po_bytes);
   w.total = off;

@@ -63,13 +63,16 @@ __device__ __forceinline__ void mfma16_settle(f32x4& x, f32x4& y) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x), "+v"(y));
 }
 
-// o[i] = o[i] * s + w * x for an accumulator held in accumulation registers.
-__device__ __forceinline__ void acc_madd(f32x16& o, int i, float s, float w, float x) {
-  float t;
-  asm("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_fmac_f32 %1, %3, %4\n\t"
-      "v_accvgpr_write_b32 %0, %1"
-      : "+a"(o[i]), "=&v"(t)
-      : "v"(s), "v"(w), "v"(x));
+// copy16_s for a base address that lane reads (VALU) just wrote into the
+// scalar registers: a vector memory instruction may read such registers only
+// five wait states after the write, and the compiler does not count them
+// for an assembly operand.
+__device__ __forceinline__ void copy16_s_after_valu(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile(
+      "s_nop 4\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(voff), "s"(base), "{m0}"(lds));
 }
 
 // Source of the rows of invisible tokens: their weights are 0, and the
@@ -128,16 +131,6 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_sparse_hg(DecodeArgs a) {
   // and the pool.  Token rows are page * 64 + (index & 63), or -1.
   // (loads from clamped, always valid addresses with the selects after
   // them: a load under a branch makes the compiler wait for it there)
-  auto load_idx = [&](int e0, int& i0, int& i1) __attribute__((always_inline)) {
-    const int ea = e0 + lane, eb = ea + 64;
-    const int va = idx_row[min(ea, e_hi - 1)], vb = idx_row[min(eb, e_hi - 1)];
-    i0 = ea < e_hi ? va : -1;
-    i1 = eb < e_hi ? vb : -1;
-  };
-  auto load_pg = [&](int i) __attribute__((always_inline)) -> int {
-    const int v = bt_row[min(max(i >> 6, 0), a.bt_stride - 1)];
-    return (i >= 0 && i < L && (i >> 6) < a.bt_stride) ? v : -1;
-  };
   auto tok_of = [&](int i, int pg) __attribute__((always_inline)) -> int {
     const bool ok = i >= 0 && i < L && (i >> 6) < a.bt_stride && pg >= 0 && pg < a.num_pages;
     return ok ? pg * kPage + (i & 63) : -1;
@@ -162,6 +155,7 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_sparse_hg(DecodeArgs a) {
     unsigned vm;        // visible tokens of the chunk (bit j: token j)
     int rope0, rope1;   // per lane: token row of RoPE copy 0 / 1
     uint32_t sa;        // LDS address of the chunk's slot
+    uint32_t alo, ahi;  // per lane: address of the latent row of lst (the zero row if invisible)
   };
   // (the token rows come in by value: a select between two variables in
   // memory would keep them there)
@@ -174,6 +168,12 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_sparse_hg(DecodeArgs a) {
     d.rope0 = __shfl(d.lst, d.lo + (lane >> 3));
     d.rope1 = __shfl(d.lst, d.lo + 8 + (lane >> 3));
     d.sa = lds_addr(slot(n));
+    // the 16 copy sources of the chunk, computed by all lanes at once: a copy
+    // then only reads its row's address out of lane lo + k
+    const uint64_t ra = d.lst >= 0 ? reinterpret_cast<uint64_t>(a.kv) + (uint64_t)(uint32_t)d.lst * kBytesBf16Row
+                                   : reinterpret_cast<uint64_t>(kZeroRow);
+    d.alo = (uint32_t)ra;
+    d.ahi = (uint32_t)(ra >> 32);
     return d;
   };
   // Copy k of a chunk: k < 16 the latent row of token k (lane = 16-byte
@@ -184,13 +184,11 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_sparse_hg(DecodeArgs a) {
     int ln = lane;
     asm volatile("" : "+v"(ln));  // per-lane offsets are not kept live through the loop
     if (k < Y::kTok) {
-      const int t = __builtin_amdgcn_readlane(d.lst, d.lo + k);
-      // the row address is wave-uniform: keep it in scalar registers
-      const uint64_t src = t >= 0 ? reinterpret_cast<uint64_t>(a.kv) + (uint64_t)t * kBytesBf16Row
-                                  : reinterpret_cast<uint64_t>(kZeroRow);
-      const uint64_t su64 = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(src >> 32)) << 32) |
-                            (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)src);
-      copy16_s(reinterpret_cast<const void*>(su64), (uint32_t)((ln ^ swz16(k)) << 4), d.sa + k * 1024);
+      // the row address is wave-uniform: two lane reads into scalar registers
+      const uint32_t lo32 = __builtin_amdgcn_readlane(d.alo, d.lo + k);
+      const uint32_t hi32 = __builtin_amdgcn_readlane(d.ahi, d.lo + k);
+      const uint64_t su64 = ((uint64_t)hi32 << 32) | lo32;
+      copy16_s_after_valu(reinterpret_cast<const void*>(su64), (uint32_t)((ln ^ swz16(k)) << 4), d.sa + k * 1024);
     } else {
       const int jb = k - Y::kTok;
       const int row = 8 * jb + (ln >> 3);
@@ -200,47 +198,54 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_sparse_hg(DecodeArgs a) {
     }
   };
 
+  // Round 0 lookups.  The block-table row is fetched towards L2 beside the
+  // index loads (into a scratch area of LDS), so the dependent page lookups
+  // find it there.  Issue order: index entries, then their pages (vector
+  // loads retire in order); the empty asm statements with a memory clobber
+  // keep the compiler from reordering the groups.
+  const int ea = e_lo + lane, eb = ea + 64;
+  int va = -1, vb = -1, pa = -1, pbg = -1;
   if (nch > 0) {
-    // Round 0 lookups and the query rows (loads in this order, so that the
-    // page lookups wait only for the index loads).
-    // The block-table row is fetched towards L2 beside the index loads (into
-    // a scratch area of LDS), so the dependent page lookups find it there.
-    {
-      const int nb = min(a.bt_stride, 1024);  // entries: up to 4 KB per row
+    const int nb = min(a.bt_stride, 1024);  // entries: up to 4 KB per row
 #pragma unroll
-      for (int k = 0; k < 4; k++) {
-        const int e = 256 * k + 64 * w + lane;
-        if (e < nb) copy4_v(bt_row + e, lds_addr(lds + Y::kLookOff + w * 1024 + k * 256));
-      }
+    for (int k = 0; k < 4; k++) {
+      const int e = 256 * k + 64 * w + lane;
+      if (e < nb) copy4_v(bt_row + e, lds_addr(lds + Y::kLookOff + w * 1024 + k * 256));
     }
-    // Issue order: index entries, their pages, then the query rows (vector
-    // loads retire in order, so the page lookups wait only for the index
-    // loads, and the query rows stay in flight while the pages are
-    // awaited).  The empty asm statements with a memory clobber keep the
-    // compiler from reordering the three groups.
-    const int ea = e_lo + lane, eb = ea + 64;
-    const int va = idx_row[min(ea, e_hi - 1)], vb = idx_row[min(eb, e_hi - 1)];
+    va = idx_row[min(ea, e_hi - 1)];
+    vb = idx_row[min(eb, e_hi - 1)];
     asm volatile("" ::: "memory");
-    const int pa = bt_row[min(max(va >> 6, 0), a.bt_stride - 1)];
-    const int pbg = bt_row[min(max(vb >> 6, 0), a.bt_stride - 1)];
+    pa = bt_row[min(max(va >> 6, 0), a.bt_stride - 1)];
+    pbg = bt_row[min(max(vb >> 6, 0), a.bt_stride - 1)];
     asm volatile("" ::: "memory");
-    {
-      const int r16 = lane & 15, g4 = lane >> 4;
+  }
+  // The group's 32 query rows, once per workgroup: 36 direct copies of whole
+  // rows (9 per wave) into slot 1 of waves 0 (rows 0..15) and 1 (rows
+  // 16..31), in the layout of a chunk, so that every wave reads its score
+  // operand out of LDS as it reads the cache rows.  Rows past the head count
+  // take row 0's query; they are never written out.
+  {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
 #pragma unroll
-      for (int rb = 0; rb < 2; rb++) {
-        // rows past the head count score with row 0's query; they are
-        // never written out
-        const int r = 16 * rb + r16;
+    for (int i = 0; i < 9; i++) {
+      const int q = 9 * w + i;  // wave-uniform
+      if (q < 32) {
+        const int rb = q >> 4, k = q & 15;
+        const size_t grow = row0 + (q < rows ? q : 0);
+        copy16_s(a.q_nope + grow * kDC, (uint32_t)((ln ^ swz16(k)) << 4),
+                 lds_addr(lds + rb * Y::kWaveBytes + Y::kSlot + k * 1024));
+      } else {
+        const int jb = q - 32, rb = jb >> 1, row = 8 * (jb & 1) + (ln >> 3);
+        const int r = 16 * rb + row;
         const size_t grow = row0 + (r < rows ? r : 0);
-        const bf16x8* qn = reinterpret_cast<const bf16x8*>(a.q_nope + grow * kDC) + g4;
-        const bf16x8* qr = reinterpret_cast<const bf16x8*>(a.q_rope + grow * kDR) + g4;
-#pragma unroll
-        for (int ks = 0; ks < 16; ks++) qf[rb][ks] = qn[4 * ks];
-#pragma unroll
-        for (int ks = 0; ks < 2; ks++) qf[rb][16 + ks] = qr[4 * ks];
+        copy16_v(reinterpret_cast<const uint8_t*>(a.q_rope + grow * kDR) + (((ln & 7) ^ ((row >> 1) & 7)) << 4),
+                 lds_addr(lds + rb * Y::kWaveBytes + Y::kSlot + Y::kABlk + (jb & 1) * 1024));
       }
     }
-    asm volatile("" ::: "memory");
+  }
+  asm volatile("" ::: "memory");
+  if (nch > 0) {
     const int i0 = ea < e_hi ? va : -1, i1 = eb < e_hi ? vb : -1;
     t0 = tok_of(i0, pa);
     t1 = tok_of(i1, pbg);
@@ -248,13 +253,32 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_sparse_hg(DecodeArgs a) {
     wait_lds();
 #pragma unroll
     for (int k = 0; k < Y::kTok + 2; k++) copy(k, d0);
-    // Take delivery of the query rows here (with chunk 0): a wait left to
-    // the compiler lands inside the loop, where it also waits for copies.
+    wait_vm<Y::kTok + 2>();  // this wave's query copies (issued before chunk 0's) have landed
+  } else {
+    wait_vm<0>();
+  }
+  __syncthreads();  // every wave's query copies are in LDS
+  if (nch > 0) {
+    const int r16 = lane & 15, g4 = lane >> 4, y = swz16(r16);
+#pragma unroll
+    for (int rb = 0; rb < 2; rb++) {
+      const uint8_t* qs = lds + rb * Y::kWaveBytes + Y::kSlot;
+#pragma unroll
+      for (int ks = 0; ks < 16; ks++)
+        qf[rb][ks] = *reinterpret_cast<const bf16x8*>(qs + r16 * 1024 + 256 * (ks >> 2) +
+                                                       64 * ((ks & 3) ^ (y >> 2)) + 16 * ((g4 ^ y) & 3));
+#pragma unroll
+      for (int k = 0; k < 2; k++)
+        qf[rb][16 + k] = *reinterpret_cast<const bf16x8*>(qs + Y::kABlk + r16 * 128 +
+                                                          (((4 * k + g4) ^ ((r16 >> 1) & 7)) << 4));
+    }
+    // take delivery here: a wait left to the compiler would land in the loop
 #pragma unroll
     for (int rb = 0; rb < 2; rb++)
 #pragma unroll
       for (int ks = 0; ks < 18; ks++) asm volatile("" : "+v"(qf[rb][ks]));
   }
+  __syncthreads();  // slot 1 of waves 0 and 1 is free for chunk 1
 
   // ------------------------------------------------------------ main loop
   unsigned vm_cur = 0;
@@ -448,13 +472,17 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_sparse_hg(DecodeArgs a) {
   const float mown = stm[32 * w + r];
   const float f = (has && mown != kNegInf) ? __builtin_amdgcn_exp2f(mown - M) / Lsum : 0.f;
   const float lse2 = has ? M + __log2f(Lsum) : kNegInf;
-  // the weight goes into the values handed to other waves as they are
-  // stored, and into the owned quarter in place
+  // The owned quarter moves to ordinary registers (the query registers are
+  // free now), weighted; the other three quarters are weighted as they are
+  // handed over.
+  float own[64];
 #pragma unroll
-  for (int i = 0; i < 4; i++) acc_scale(o[i], f);
+  for (int jj = 0; jj < 4; jj++)
+#pragma unroll
+    for (int e = 0; e < 16; e++) own[16 * jj + e] = acc_get(o[jj], e) * f;
 
-  // 4 slots from SB to `buf` (4 KB per slot, 1 KB of consecutive bytes per
-  // store), or added from `buf` into slots 0..3
+  // slots SB..SB+3 to `buf` (4 KB per slot, 1 KB of consecutive bytes per
+  // store) times sc
   auto put4 = [&](auto SB, float* buf, float sc) __attribute__((always_inline)) {
     constexpr int sb = decltype(SB)::value;
 #pragma unroll
@@ -465,23 +493,19 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_sparse_hg(DecodeArgs a) {
             f32x4{acc_get(o[sb + jj], 4 * q), acc_get(o[sb + jj], 4 * q + 1), acc_get(o[sb + jj], 4 * q + 2),
                   acc_get(o[sb + jj], 4 * q + 3)} * sc;
   };
-  auto add4 = [&](const float* buf, float keep, float wt) __attribute__((always_inline)) {
-#pragma unroll
-    for (int jj = 0; jj < 4; jj++)
-#pragma unroll
-      for (int q = 0; q < 4; q++) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(buf + (jj * 4 + q) * 256 + lane * 4);
-#pragma unroll
-        for (int e = 0; e < 4; e++) acc_madd(o[jj], 4 * q + e, keep, wt, v[e]);
-      }
-  };
   float* const X = reinterpret_cast<float*>(lds);  // two regions of 4 x 16 KB
   unroll<3>([&](auto K) __attribute__((always_inline)) {
     constexpr int k = decltype(K)::value + 1;
     float* const reg = X + ((k & 1) ? 0 : 16384);
     put4(std::integral_constant<int, 4 * k>{}, reg + 4096 * ((w + k) & 3), f);
     __syncthreads();
-    add4(reg + 4096 * w, 1.f, 1.f);
+    const float* buf = reg + 4096 * w;
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(buf + i * 256 + lane * 4);
+#pragma unroll
+      for (int e = 0; e < 4; e++) own[4 * i + e] += v[e];
+    }
   });
 
   // ------------------------------------------------------------ results
@@ -494,8 +518,9 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_sparse_hg(DecodeArgs a) {
     for (int jj = 0; jj < 4; jj++) {
 #pragma unroll
       for (int q = 0; q < 4; q++) {
-        bf16x2 p0 = {(__bf16)(acc_get(o[jj], 4 * q + 0) * inv), (__bf16)(acc_get(o[jj], 4 * q + 1) * inv)};
-        bf16x2 p1 = {(__bf16)(acc_get(o[jj], 4 * q + 2) * inv), (__bf16)(acc_get(o[jj], 4 * q + 3) * inv)};
+        const float* x = own + 16 * jj + 4 * q;
+        bf16x2 p0 = {(__bf16)(x[0] * inv), (__bf16)(x[1] * inv)};
+        bf16x2 p1 = {(__bf16)(x[2] * inv), (__bf16)(x[3] * inv)};
         *reinterpret_cast<u32x2*>(dst + 32 * jj + 8 * q) =
             u32x2{__builtin_bit_cast(unsigned, p0), __builtin_bit_cast(unsigned, p1)};
       }
@@ -508,16 +533,31 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_sparse_hg(DecodeArgs a) {
   }
 
   // Several ranges: store this range's normalised partial (each wave its
-  // quarter, in fragment order) and its log2-sum-exp; combine_hg merges them.
+  // quarter, in fragment order) as fp16 divided by the row's largest
+  // magnitude in the quarter (so every value lies in [-1, 1]), that scale,
+  // and the range's log2-sum-exp; combine_hg merges them.
+  float mx = 0.f;
+#pragma unroll
+  for (int i = 0; i < 64; i++) mx = fmaxf(mx, fabsf(own[i]));
+  mx = pair_max(mx);  // lanes r and r + 32 hold the row's other dims
+  const float sc = mx > 0.f ? mx : 1.f;
+  const float inv = 1.0f / sc;
   const size_t part = (size_t)item * S + split;
-  put4(std::integral_constant<int, 0>{}, a.ws_po + part * (16 * 1024) + w * 4096, 1.f);
+  _Float16* const pdst = reinterpret_cast<_Float16*>(a.ws_po) + part * (16 * 1024) + w * 4096;
+#pragma unroll
+  for (int i = 0; i < 16; i++)
+    *reinterpret_cast<f16x4*>(pdst + i * 256 + lane * 4) =
+        f16x4{(_Float16)(own[4 * i] * inv), (_Float16)(own[4 * i + 1] * inv), (_Float16)(own[4 * i + 2] * inv),
+              (_Float16)(own[4 * i + 3] * inv)};
+  if (lane < 32) a.ws_psc[part * 128 + w * 32 + r] = sc;
   if (w == 0 && lane < 32) a.ws_plse[part * 32 + r] = lse2;
 }
 
 // Merge of the ranges of every item, in range order: thread t of the item's
-// 4096 handles the 16-byte piece t of the partials (fragment order: slot
-// t >> 8 = dim block, (t >> 6) & 3 = 8-dim group, t & 63 = lane), i.e. row
-// t & 31 and dims 32 (t >> 8) + 8 ((t >> 6) & 3) + 4 ((t >> 5) & 1) .. +3.
+// 4096 handles the four values t of the partials (fragment order: t >> 10 =
+// the wave that stored them, t >> 8 = dim block, (t >> 6) & 3 = 8-dim group,
+// t & 63 = lane), i.e. row t & 31 and dims
+// 32 (t >> 8) + 8 ((t >> 6) & 3) + 4 ((t >> 5) & 1) .. +3.
 __global__ __launch_bounds__(256) void combine_hg(DecodeArgs a) {
   const int item = blockIdx.x;
   const int t = blockIdx.y * 256 + threadIdx.x;
@@ -540,10 +580,13 @@ __global__ __launch_bounds__(256) void combine_hg(DecodeArgs a) {
   }
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
+  const _Float16* const po = reinterpret_cast<const _Float16*>(a.ws_po);
+  const int qw = t >> 10;  // the quarter of the dims (the wave that stored it)
   for (int s = 0; s < S; s++) {
     const float ws = __builtin_amdgcn_exp2f(a.ws_plse[(base + s) * 32 + r] - mx);  // 0: empty range
-    const f32x4 v = *reinterpret_cast<const f32x4*>(a.ws_po + (base + s) * (16 * 1024) + 4 * t);
-    acc += ws * v;
+    const f16x4 h = *reinterpret_cast<const f16x4*>(po + (base + s) * (16 * 1024) + 4 * t);
+    const float f = ws * a.ws_psc[(base + s) * 128 + qw * 32 + r];
+    acc += f * f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
     wsum += ws;
   }
   const float inv = 1.0f / wsum;

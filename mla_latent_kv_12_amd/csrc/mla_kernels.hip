@@ -118,7 +118,7 @@ struct Wide {
   static constexpr int kDummyOff = kMrgOff + 2 * 32 * R * 4;
   static constexpr int kLdsBytes = kDummyOff + 64;
   static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
-  static_assert(4 * (2 * (kFoldUnits + 1) + kThreads) <= kSlots * kABlk,
+  static_assert(4 * 2 * (kFoldUnits + 1) <= kSlots * kABlk,
                 "the self-schedule's scratch fits in the chunk ring");
   static_assert(kABlk % 1024 == 0 && kBBlk % 16 == 0 && kBOff % 16 == 0, "block alignment");
   // vector-memory operations wave w issues per step: its copies, plus the
@@ -167,7 +167,7 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
   // still free) unless a scheduling launch already wrote it.
   WgSched sc;
   if (a.fold_plan) {
-    sc = sched_in_wg<SPARSE>(a, reinterpret_cast<int*>(lds), W::kThreads, tid, wg);
+    sc = sched_in_wg<SPARSE>(a, reinterpret_cast<int*>(lds), tid, wg);
   } else {
     sc.u0 = ldc(a.ws_work + 2 * wg);
     sc.t0 = ldc(a.ws_work + 2 * wg + 1);

@@ -159,68 +159,69 @@ __device__ __forceinline__ void unit_splits(int c, int n, int q, int* ns, int* g
   *ns = (c + kSplitCost + n - 1) / q - *gf + 1;
 }
 
+// Inclusive prefix sum of x over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
 // Units the main pass schedules for itself (up to kFoldUnits), in the LDS
-// it has not started using yet (2 (U + 1) + nthr ints), instead of reading
-// a separate scheduling launch's output: every workgroup computes the same
+// it has not started using yet (2 (U + 1) ints), instead of reading a
+// separate scheduling launch's output: every workgroup computes the same
 // cost prefix and finds its own share, and the workgroup whose share holds
 // a unit's cost position writes that unit's metadata for the split merge.
-
+// Wave 0 does the prefix sums with lane shuffles (each lane takes a run of
+// consecutive units), so the other waves wait at a single barrier.
 template <bool SPARSE>
-__device__ WgSched sched_in_wg(const DecodeArgs& a, int* scr, int nthr, int tid, int wg) {
+__device__ WgSched sched_in_wg(const DecodeArgs& a, int* scr, int tid, int wg) {
   const int U = a.n_units, G = a.num_wg;
   int* const C = scr;           // [U + 1] cost prefix
   int* const NS = C + U + 1;    // [U + 1] prefix of split counts
-  int* const part = NS + U + 1; // [nthr]
-  const int per = (U + nthr - 1) / nthr;
-  const int lo = min(U, tid * per), hi = min(U, lo + per);
-  auto scan = [&](int v) -> int {  // inclusive prefix of v over the threads
-    part[tid] = v;
-    __syncthreads();
-    for (int off = 1; off < nthr; off <<= 1) {
-      const int w = tid >= off ? part[tid - off] : 0;
-      __syncthreads();
-      part[tid] += w;
-      __syncthreads();
+  if (tid < 64) {
+    const int lane = tid;
+    const int per = (U + 63) / 64;
+    const int lo = min(U, lane * per), hi = min(U, lo + per);
+    int s = 0;
+    for (int u = lo; u < hi; u++) s += unit_tiles(a, SPARSE, u) + kSplitCost;
+    const int incl = wave_incl_scan(s, lane);
+    const int total = __shfl(incl, 63, 64);
+    int run = incl - s;
+    for (int u = lo; u < hi; u++) {
+      C[u] = run;
+      run += unit_tiles(a, SPARSE, u) + kSplitCost;
     }
-    const int r = part[tid];
-    __syncthreads();
-    return r;
-  };
-  int s = 0;
-  for (int u = lo; u < hi; u++) s += unit_tiles(a, SPARSE, u) + kSplitCost;
-  const int incl = scan(s);
-  int run = incl - s;
-  for (int u = lo; u < hi; u++) {
-    C[u] = run;
-    run += unit_tiles(a, SPARSE, u) + kSplitCost;
+    if (lane == 63) C[U] = total;
+    const int q = max((total + G - 1) / G, kMinWgCost);
+    int ns_sum = 0;
+    for (int u = lo; u < hi; u++) {
+      int ns, gf;
+      unit_splits(C[u], C[u + 1] - C[u] - kSplitCost, q, &ns, &gf);
+      ns_sum += ns;
+    }
+    const int ns_incl = wave_incl_scan(ns_sum, lane);
+    int base = ns_incl - ns_sum;
+    for (int u = lo; u < hi; u++) {
+      const int n = C[u + 1] - C[u] - kSplitCost;
+      int ns, gf;
+      unit_splits(C[u], n, q, &ns, &gf);
+      NS[u] = base;
+      if (C[u] / q == wg) {  // one writer per unit
+        a.ws_meta[4 * u + 0] = n;
+        a.ws_meta[4 * u + 1] = base;
+        a.ws_meta[4 * u + 2] = ns;
+        a.ws_meta[4 * u + 3] = gf;
+      }
+      base += ns;
+    }
+    if (lane == 63) NS[U] = ns_incl;
   }
-  if (tid == nthr - 1) C[U] = incl;
   __syncthreads();
   const int total = C[U];
   const int q = max((total + G - 1) / G, kMinWgCost);
-  int ns_sum = 0;
-  for (int u = lo; u < hi; u++) {
-    int ns, gf;
-    unit_splits(C[u], C[u + 1] - C[u] - kSplitCost, q, &ns, &gf);
-    ns_sum += ns;
-  }
-  const int ns_incl = scan(ns_sum);
-  int base = ns_incl - ns_sum;
-  for (int u = lo; u < hi; u++) {
-    const int n = C[u + 1] - C[u] - kSplitCost;
-    int ns, gf;
-    unit_splits(C[u], n, q, &ns, &gf);
-    NS[u] = base;
-    if (C[u] / q == wg) {  // one writer per unit
-      a.ws_meta[4 * u + 0] = n;
-      a.ws_meta[4 * u + 1] = base;
-      a.ws_meta[4 * u + 2] = ns;
-      a.ws_meta[4 * u + 3] = gf;
-    }
-    base += ns;
-  }
-  if (tid == nthr - 1) NS[U] = ns_incl;
-  __syncthreads();
   // this workgroup's share [wg q, (wg + 1) q) of the cost line
   auto locate = [&](long long x, int* u, int* t) {
     if (x >= total) {

@@ -7,10 +7,11 @@
 //   q_nope[m, h, :] = q_c[m, h, :] . W_UK[h]          (128 -> 512, per head)
 //   out, lse        = absorbed decode over the latent cache
 //   o[m, h, :]      = W_UV[h] . out[m, h, :]           (512 -> 128, per head)
-// One op at a time it is five launches: absorb, split-KV schedule, main pass,
-// split merge, projection.  The schedule only reads the sequence lengths, so
-// here it runs as one more workgroup of the absorption launch
-// (absorb_plan_kernel), beside the GEMM instead of before it.  The other
+// One op at a time it is four launches: absorb, main pass (computing its
+// own split-KV schedule first), split merge, projection.  The schedule only
+// reads the sequence lengths, so here it runs as one more workgroup of the
+// absorption launch (absorb_plan_kernel), beside the GEMM, and the main
+// pass reads its share instead of computing it.  The other
 // steps stay separate launches on purpose: the absorption and the
 // projection read each head's weights once only when a workgroup covers the
 // rows of one head over the whole batch, while the main pass and the split

@@ -208,11 +208,12 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) 
 #pragma unroll
         for (int i = 0; i < 16; i++) mloc = fmaxf(mloc, s2[hf][i]);
       } else {
+        // the row sees tokens up to lim (none when the row is past T);
+        // token k0 + 32 hf + 8 (i / 4) + 4 g + i % 4 against it
+        const int lim = (row_ok ? (a.causal ? min(row, T - 1) : T - 1) : -1) - (k0 + 32 * hf + 4 * g);
 #pragma unroll
         for (int i = 0; i < 16; i++) {
-          const int tok = k0 + 32 * hf + 8 * (i / 4) + 4 * g + (i % 4);
-          const bool ok = row_ok && tok < T && (!a.causal || tok <= row);
-          s2[hf][i] = ok ? s2[hf][i] : kNegInf;
+          s2[hf][i] = 8 * (i / 4) + (i % 4) <= lim ? s2[hf][i] : kNegInf;
           mloc = fmaxf(mloc, s2[hf][i]);
         }
       }
@@ -234,8 +235,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) 
       float pv[16];
 #pragma unroll
       for (int i = 0; i < 16; i++) {
-        const float x = s2[hf][i];
-        pv[i] = x == kNegInf ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(x, c2, -muse));
+        // a masked score is -inf, and exp2(-inf) = 0 (muse is finite)
+        pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s2[hf][i], c2, -muse));
         psum += pv[i];
       }
 #pragma unroll

@@ -167,6 +167,31 @@ def test_plan_once_then_planned_calls():
     check(out1, lse1, ref[0], ref[1], "planned", nvis=visible_counts(inp))
 
 
+@pytest.mark.parametrize("B", [65, 200, 2048, 2049])
+@pytest.mark.parametrize("num_wg", [0, 7, 300])
+def test_self_schedule_matches_the_scheduling_launch(B, num_wg):
+    """A decode of up to 2048 units computes its split-KV schedule inside the
+    main pass (each lane of one wave takes a run of consecutive units past 64
+    units); the same call after mla_plan reads the scheduling launch's output
+    instead.  Both must give the same splits and so bit-identical results.
+    2049 units is past the in-pass limit: both calls use the launch."""
+    g = torch.Generator().manual_seed(B + num_wg)
+    lens = tuple(int(x) for x in torch.randint(0, 129, (B,), generator=g))
+    inp = custom(B=B, H=16, lens=lens, seed=B)
+    d = dev(inp)
+    m = mla()
+    ws = m.alloc_workspace(B, 1, 16, num_wg=num_wg)
+    a = run(d, num_wg=num_wg, workspace=ws)
+    a = (a[0].clone(), a[1].clone())
+    m.plan(d["cache_seqlens"], B, 1, 16, ws, num_wg=num_wg)
+    b = run(d, num_wg=num_wg, planned=True, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1]), "schedules differ"
+    if B == 65:
+        ref = oracle.decode(inp)
+        check(a[0], a[1], ref[0], ref[1], f"self-scheduled B={B} num_wg={num_wg}", nvis=visible_counts(inp))
+
+
 @pytest.mark.parametrize("name", ["dsv3_decode", "fp8_head_slice", "dsa_sparse"])
 def test_graph_replay_matches_eager(name):
     """The three calls (plan, main pass, combine) captured into one HIP graph:

@@ -37,7 +37,8 @@ __global__ __launch_bounds__(256) void absorb_plan_kernel(LayerArgs la) {
     plan_work<false>(la.d);
     return;
   }
-  const int j = i - 1;
+  // the GEMM's workgroups of one head on one XCD (see head_gemm_kernel)
+  const int j = xcd_logical(i - 1, gridDim.x - 1);
   const int H = la.pa.H;
   head_gemm<kDHead, kDC, 1>(la.pa, j & 3, (j >> 2) % H, (j >> 2) / H);
 }

@@ -16,6 +16,7 @@
 // head over up to 128 rows m with bf16 MFMA 32x32x16 and fp32 accumulation;
 // its weight fragments stay in registers while it walks the row tiles, so
 // every weight byte is read from HBM once.
+#include "mla_device.h"
 #include "mla_internal.h"
 #include "mla_proj.h"
 
@@ -23,9 +24,14 @@ namespace mla {
 namespace kern {
 namespace {
 
+// One workgroup per (column tile group, head, row block) on a flat grid;
+// the workgroups of one head are consecutive logical workgroups of one XCD,
+// so the activation rows that all of them read meet in that XCD's L2.
 template <int K, int N, int SPLIT>
 __global__ __launch_bounds__(256) void head_gemm_kernel(ProjArgs a) {
-  head_gemm<K, N, SPLIT>(a, blockIdx.x, blockIdx.y, blockIdx.z);
+  constexpr int NX = N / (32 * 4 / SPLIT);  // column tile groups per head
+  const int lid = xcd_logical(blockIdx.x, gridDim.x);
+  head_gemm<K, N, SPLIT>(a, lid % NX, (lid / NX) % a.H, lid / (NX * a.H));
 }
 
 }  // namespace
@@ -35,10 +41,10 @@ __global__ __launch_bounds__(256) void head_gemm_kernel(ProjArgs a) {
 hipError_t launch_proj(const ProjArgs& a, bool absorb, hipStream_t stream) {
   const unsigned mblocks = (unsigned)((a.M + kern::kRowsPerBlock - 1) / kern::kRowsPerBlock);
   if (absorb)  // K = 128, N = 512
-    hipLaunchKernelGGL((kern::head_gemm_kernel<kDHead, kDC, 1>), dim3(kDC / 128, a.H, mblocks), dim3(256),
+    hipLaunchKernelGGL((kern::head_gemm_kernel<kDHead, kDC, 1>), dim3((kDC / 128) * a.H * mblocks), dim3(256),
                        0, stream, a);
   else         // K = 512, N = 128
-    hipLaunchKernelGGL((kern::head_gemm_kernel<kDC, kDHead, 4>), dim3(kDHead / 32, a.H, mblocks), dim3(256),
+    hipLaunchKernelGGL((kern::head_gemm_kernel<kDC, kDHead, 4>), dim3((kDHead / 32) * a.H * mblocks), dim3(256),
                        0, stream, a);
   return hipGetLastError();
 }

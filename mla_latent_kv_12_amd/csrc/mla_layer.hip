@@ -30,8 +30,9 @@ namespace mla {
 namespace kern {
 
 // Grid: one scheduling workgroup (block 0), then 4 x H x ceil(M / 128)
-// absorption workgroups (column tile of 128, head, row block).
+// absorption workgroups (128 columns, head, row block of 128).
 __global__ __launch_bounds__(256) void absorb_plan_kernel(LayerArgs la) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int i = blockIdx.x;
   if (i == 0) {
     plan_work<false>(la.d);
@@ -40,15 +41,20 @@ __global__ __launch_bounds__(256) void absorb_plan_kernel(LayerArgs la) {
   // the GEMM's workgroups of one head on one XCD (see head_gemm_kernel)
   const int j = xcd_logical(i - 1, gridDim.x - 1);
   const int H = la.pa.H;
-  head_gemm<kDHead, kDC, 1>(la.pa, j & 3, (j >> 2) % H, (j >> 2) / H);
+  head_gemm<kDHead, kDC, 1>(la.pa, lds, j & 3, (j >> 2) % H, (j >> 2) / H);
 }
 
 }  // namespace kern
 
 hipError_t launch_absorb_plan(const LayerArgs& la, hipStream_t stream) {
-  const long long mblocks = (la.pa.M + kern::kRowsPerBlock - 1) / kern::kRowsPerBlock;
+  using T = kern::ProjTile<kDHead, kDC, 1>;
+  static_assert(kDC / T::kCols == 4, "four column tiles per head");
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern::absorb_plan_kernel),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, T::kLdsBytes);
+  if (e != hipSuccess) return e;
+  const long long mblocks = (la.pa.M + T::kRows - 1) / T::kRows;
   const long long grid = 1 + 4LL * la.pa.H * mblocks;
-  hipLaunchKernelGGL(kern::absorb_plan_kernel, dim3((unsigned)grid), dim3(256), 0, stream, la);
+  hipLaunchKernelGGL(kern::absorb_plan_kernel, dim3((unsigned)grid), dim3(256), T::kLdsBytes, stream, la);
   return hipGetLastError();
 }
 

@@ -11,69 +11,103 @@ namespace kern {
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kRowsPerBlock = 128;
-
 // K: contraction length, N: output columns per head, SPLIT: waves that
 // share one 32-column tile, each taking 1/SPLIT of the contraction (their
 // partial tiles are summed through LDS).  A workgroup of 4 waves computes
-// 4/SPLIT tiles of 32 columns of one head for up to 128 rows.  The long
-// contraction (K = 512) is split 4 ways: four times the waves of one wave
-// per tile, and a quarter of the dependent load chain per wave.
+// 4/SPLIT tiles of 32 columns of one head for a block of rows.  The long
+// contraction (K = 512) is split 4 ways.
 template <int K, int N, int SPLIT>
-__device__ __forceinline__ void head_gemm(const ProjArgs& a, int bx, int h, int bz) {
-  __shared__ float red[SPLIT > 1 ? 3 : 1][16][64];  // partial tiles of the non-leading waves
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+struct ProjTile {
+  static constexpr int kCols = 32 * 4 / SPLIT;      // columns per workgroup
+  static constexpr int kRows = SPLIT > 1 ? 64 : 128;  // rows per row block
+  static constexpr int kRowBytes = 2 * K;           // one weight or activation row
+  static constexpr int kWBytes = kCols * kRowBytes; // the weight tile
+  static constexpr int kABytes = kRows * kRowBytes; // the activation tile
+  static constexpr int kRedOff = kWBytes + kABytes; // partial tiles of the non-leading waves
+  static constexpr int kLdsBytes = kRedOff + (SPLIT > 1 ? 3 * 16 * 64 * 4 : 0);
+  static constexpr int kCopies = (kWBytes + kABytes) / 1024;
+  static_assert(kRowBytes <= 1024 && 1024 % kRowBytes == 0 && kCopies % 4 == 0, "copy shape");
+  static_assert(kLdsBytes <= 128 * 1024, "LDS budget");
+};
+
+// Both tiles are staged in LDS by direct copies of whole rows (1 KB per
+// copy: a weight or activation row is 256 B or 1 KB, contiguous in HBM), so
+// every HBM read is fully coalesced; 16-byte chunk c of tile row r sits at
+// position c ^ (r & 15), so that the MFMA operand reads (one chunk of 16
+// consecutive rows per 16 lanes) cover every bank.  `lds` is the dynamic
+// LDS of the launch, ProjTile<K, N, SPLIT>::kLdsBytes bytes.
+template <int K, int N, int SPLIT>
+__device__ __forceinline__ void head_gemm(const ProjArgs& a, uint8_t* lds, int bx, int h, int bz) {
+  using T = ProjTile<K, N, SPLIT>;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, g = lane >> 5;
-  const int part = wave % SPLIT;               // which share of the contraction
-  const int n0 = (bx * (4 / SPLIT) + wave / SPLIT) * 32;
-  const int m_base = bz * kRowsPerBlock;
   const int H = a.H, M = a.M;
-  constexpr int KW = K / SPLIT;
-  constexpr int KS = KW / 16;
-  const int k_off = part * KW;
-  // weight fragments: row n0 + l32 of Bt[h], k = k_off + 16 ks + 8 g .. + 7
-  bf16x8 wf[KS];
-  const bf16x8* wrow = reinterpret_cast<const bf16x8*>(a.w + ((size_t)h * N + n0 + l32) * K + k_off + 8 * g);
+  const int n_base = bx * T::kCols, m_base = bz * T::kRows;
+  constexpr int kChunks = K / 8, kRowsPerCopy = 1024 / T::kRowBytes;
+  {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int rr = ln / kChunks, p = ln % kChunks;  // row within the copy, LDS chunk position
 #pragma unroll
-  for (int ks = 0; ks < KS; ks++) wf[ks] = wrow[2 * ks];
-  // every row tile's activations are requested together with the weights:
-  // one memory round trip for the whole workgroup
-  constexpr int kMT = kRowsPerBlock / 32;
-  bf16x8 av_all[kMT][KS];
-#pragma unroll
-  for (int mt = 0; mt < kMT; mt++) {
-    const int m0 = m_base + 32 * mt;
-    const int row = m0 + l32;
-    const bool ok = m0 < M && row < M;
-    const bf16x8* arow =
-        reinterpret_cast<const bf16x8*>(a.a + ((size_t)(ok ? row : 0) * H + h) * K + k_off + 8 * g);
-#pragma unroll
-    for (int ks = 0; ks < KS; ks++) av_all[mt][ks] = ok ? arow[2 * ks] : bf16x8{};
+    for (int i = 0; i < T::kCopies / 4; i++) {
+      const int cpy = 4 * i + wave;
+      const uint8_t* src;
+      int row;
+      if (cpy < T::kWBytes / 1024) {
+        row = cpy * kRowsPerCopy + rr;
+        src = reinterpret_cast<const uint8_t*>(a.w + ((size_t)h * N + n_base + row) * K);
+      } else {
+        const int r0 = (cpy - T::kWBytes / 1024) * kRowsPerCopy;
+        if (m_base + r0 >= M) continue;  // (wave-uniform) rows past M are never read
+        row = r0 + rr;
+        const int m = min(m_base + row, M - 1);  // rows past M are never stored
+        src = reinterpret_cast<const uint8_t*>(a.a + ((size_t)m * H + h) * K);
+      }
+      copy16_v(src + ((p ^ (row & 15)) << 4), lds_addr(lds + cpy * 1024));
+    }
   }
+  wait_vm<0>();
+  __syncthreads();
+
+  const int part = wave % SPLIT;               // which share of the contraction
+  const int col0 = (wave / SPLIT) * 32;        // the wave's columns within the tile
+  constexpr int KS = K / SPLIT / 16;           // k-steps per wave
+  const int kc0 = part * (K / SPLIT / 8);      // first chunk of the wave's share
+  const int wr = col0 + l32;                   // weight tile row of this lane
+  bf16x8 wf[KS];
 #pragma unroll
-  for (int mt = 0; mt < kMT; mt++) {
+  for (int ks = 0; ks < KS; ks++)
+    wf[ks] = *reinterpret_cast<const bf16x8*>(lds + wr * T::kRowBytes + (((kc0 + 2 * ks + g) ^ (wr & 15)) << 4));
+  float* const red = reinterpret_cast<float*>(lds + T::kRedOff);
+#pragma unroll
+  for (int mt = 0; mt < T::kRows / 32; mt++) {
     const int m0 = m_base + 32 * mt;
     if (m0 >= M) break;  // uniform over the workgroup
+    const int ar = 32 * mt + l32;              // activation tile row of this lane
     const int row = m0 + l32;
     const bool ok = row < M;
-    const bf16x8* av = av_all[mt];
     f32x16 acc = {};
 #pragma unroll
-    for (int ks = 0; ks < KS; ks++) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[ks], av[ks], acc, 0, 0, 0);
+    for (int ks = 0; ks < KS; ks++) {
+      const bf16x8 af = *reinterpret_cast<const bf16x8*>(lds + T::kWBytes + ar * T::kRowBytes +
+                                                         (((kc0 + 2 * ks + g) ^ (ar & 15)) << 4));
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[ks], af, acc, 0, 0, 0);
+    }
     if constexpr (SPLIT > 1) {
       if (part > 0) {
 #pragma unroll
-        for (int r = 0; r < 16; r++) red[part - 1][r][lane] = acc[r];
+        for (int r = 0; r < 16; r++) red[((part - 1) * 16 + r) * 64 + lane] = acc[r];
       }
       __syncthreads();
       if (part == 0) {
 #pragma unroll
-        for (int r = 0; r < 16; r++) acc[r] += red[0][r][lane] + red[1][r][lane] + red[2][r][lane];
+        for (int r = 0; r < 16; r++)
+          acc[r] += red[r * 64 + lane] + red[(16 + r) * 64 + lane] + red[(32 + r) * 64 + lane];
       }
     }
-    // lane holds column m = row, rows n = n0 + 8 q + 4 g + i (i < 4) of D^T
+    // lane holds column m = row, rows n = n_base + col0 + 8 q + 4 g + i (i < 4) of D^T
     if (part == 0 && ok) {
-      __bf16* crow = reinterpret_cast<__bf16*>(a.c) + ((size_t)row * H + h) * N + n0 + 4 * g;
+      __bf16* crow = reinterpret_cast<__bf16*>(a.c) + ((size_t)row * H + h) * N + n_base + col0 + 4 * g;
 #pragma unroll
       for (int q = 0; q < 4; q++) {
         bf16x4 v = {(__bf16)acc[4 * q], (__bf16)acc[4 * q + 1], (__bf16)acc[4 * q + 2], (__bf16)acc[4 * q + 3]};

@@ -29,9 +29,22 @@ namespace {
 // so the activation rows that all of them read meet in that XCD's L2.
 template <int K, int N, int SPLIT>
 __global__ __launch_bounds__(256) void head_gemm_kernel(ProjArgs a) {
-  constexpr int NX = N / (32 * 4 / SPLIT);  // column tile groups per head
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  constexpr int NX = N / ProjTile<K, N, SPLIT>::kCols;  // column tiles per head
   const int lid = xcd_logical(blockIdx.x, gridDim.x);
-  head_gemm<K, N, SPLIT>(a, lid % NX, (lid / NX) % a.H, lid / (NX * a.H));
+  head_gemm<K, N, SPLIT>(a, lds, lid % NX, (lid / NX) % a.H, lid / (NX * a.H));
+}
+
+template <int K, int N, int SPLIT>
+hipError_t launch_head_gemm(const ProjArgs& a, hipStream_t stream) {
+  using T = ProjTile<K, N, SPLIT>;
+  const void* f = reinterpret_cast<const void*>(head_gemm_kernel<K, N, SPLIT>);
+  hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, T::kLdsBytes);
+  if (e != hipSuccess) return e;
+  const long long mblocks = (a.M + T::kRows - 1) / T::kRows;
+  hipLaunchKernelGGL((head_gemm_kernel<K, N, SPLIT>), dim3((unsigned)((N / T::kCols) * a.H * mblocks)), dim3(256),
+                     T::kLdsBytes, stream, a);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -39,14 +52,8 @@ __global__ __launch_bounds__(256) void head_gemm_kernel(ProjArgs a) {
 
 
 hipError_t launch_proj(const ProjArgs& a, bool absorb, hipStream_t stream) {
-  const unsigned mblocks = (unsigned)((a.M + kern::kRowsPerBlock - 1) / kern::kRowsPerBlock);
-  if (absorb)  // K = 128, N = 512
-    hipLaunchKernelGGL((kern::head_gemm_kernel<kDHead, kDC, 1>), dim3((kDC / 128) * a.H * mblocks), dim3(256),
-                       0, stream, a);
-  else         // K = 512, N = 128
-    hipLaunchKernelGGL((kern::head_gemm_kernel<kDC, kDHead, 4>), dim3((kDHead / 32) * a.H * mblocks), dim3(256),
-                       0, stream, a);
-  return hipGetLastError();
+  if (absorb) return kern::launch_head_gemm<kDHead, kDC, 1>(a, stream);  // K = 128, N = 512
+  return kern::launch_head_gemm<kDC, kDHead, 4>(a, stream);            // K = 512, N = 128
 }
 
 }  // namespace mla

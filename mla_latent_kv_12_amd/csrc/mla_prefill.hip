@@ -9,61 +9,46 @@
 //   lse = ln sum_j exp(scale q_t . k_j).
 //
 // One workgroup per (256 query rows, head, sequence); wave w owns rows
-// 32w..32w+31 with their Q in registers.  K/V tiles of 64 tokens are staged in
-// LDS by the whole workgroup (K row-padded, V stored transposed so that the
-// P.V operand reads are contiguous).  Per tile and wave: S^T = K Q^T with bf16
-// MFMA 32x32x16 over 192 dims, an online softmax in the log2 domain, P moved
-// into the MFMA operand layout by lane swaps in registers, and O^T += V^T P^T
-// (fp32 accumulation).  Tiles entirely above a wave's rows are
+// 32w..32w+31 with their Q in registers.  K/V tiles of 64 tokens are copied
+// HBM -> LDS by the whole workgroup with direct copies of whole rows (5 per
+// wave and tile), two tiles ahead of their use, into rings of 3 (K) and 4
+// (V) buffers; rows are XOR-swizzled in 16-byte chunks for the operand
+// reads.  Per tile and wave: S^T = K Q^T with bf16 MFMA 32x32x16 over 192
+// dims, an online softmax in the log2 domain, and O^T += V^T P^T (fp32
+// accumulation), V^T read by the transposing LDS read so that each lane's
+// softmax weights are already its P operand.  The P.V of tile j - 1 runs in
+// step j beside tile j's softmax.  Tiles entirely above a wave's rows are
 // skipped under the causal rule.
+#include "mla_device.h"
 #include "mla_internal.h"
-
-#include <utility>
 
 namespace mla {
 namespace kern {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kDqk = 192, kDv = 128;
 constexpr int kWaves = 8, kRowsWg = 32 * kWaves, kTile = 64;
-constexpr int kKStride = 200;  // bf16 elements per K row in LDS (400 B, 16-byte aligned, padded)
-constexpr int kVStride = 72;   // bf16 elements per V^T row (64 tokens + pad)
-constexpr float kNegInf = -__builtin_inff();
 constexpr float kLog2e = 1.44269504088896340736f;
-constexpr float kLn2 = 0.693147180559945309f;
+constexpr int kKRow = 2 * kDqk, kVRow = 2 * kDv;  // bytes per K / V row
+constexpr int kKBuf = kTile * kKRow, kVBuf = kTile * kVRow;
+constexpr int kNK = 3, kNV = 4;                   // ring buffers
+constexpr int kVOff = kNK * kKBuf;
+constexpr int kLdsBytes = kVOff + kNV * kVBuf;
+constexpr int kKCopies = kKBuf / 1024, kVCopies = kVBuf / 1024;
+constexpr int kPerWave = (kKCopies + kVCopies) / kWaves;  // copies per wave and tile
+static_assert((kKCopies + kVCopies) % kWaves == 0 && kLdsBytes <= 160 * 1024, "tile shape");
 
-// K operand reads issued from assembly with explicit counted waits, so that
-// several are in flight per MFMA (the compiler keeps about two).  At the
-// start of a tile's scores no other LDS operation of the wave is pending
-// (the workgroup barrier drained them), so the counts are exact.
-template <int OFF>
-__device__ __forceinline__ void lds_rd16(bf16x8& dst, uint32_t addr) {
-  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(dst) : "v"(addr), "n"(OFF));
-}
-template <int N>
-__device__ __forceinline__ void lds_ready(bf16x8& v) {
-  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(v) : "n"(N));
-}
-template <typename F, int... I>
-__device__ __forceinline__ void unroll_impl(F&& f, std::integer_sequence<int, I...>) {
-  (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, typename F>
-__device__ __forceinline__ void unroll(F&& f) {
-  unroll_impl(f, std::make_integer_sequence<int, N>{});
-}
+// K row r: 16-byte chunk c at position c ^ ((r >> 1) & 7) (the 16 rows of an
+// operand read then cover every bank: a 384-byte row shifts the banks by
+// half a row).  V row r: chunk c at position c ^ sw16(r & 15), the layout the
+// transposing read below expects.
+__device__ __forceinline__ int ksw(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int sw16(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
 __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) {
-  // three buffers: tile j + 1 is stored while tile j (scores) and tile
-  // j - 1 (its P.V, pipelined into step j) are read
-  __shared__ __attribute__((aligned(16))) __bf16 k_lds2[3][kTile * kKStride];
-  __shared__ __attribute__((aligned(16))) __bf16 vt_lds2[3][kDv * kVStride];
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, g = lane >> 5;
   // the last query tiles see the most keys: dispatch them first
@@ -73,120 +58,135 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) 
   const size_t seq = (size_t)b * T;
   const int row = t0 + 32 * wave + l32;  // this lane's query position
   const bool row_ok = row < T;
+  const int last = a.causal ? min(T - 1, t0 + kRowsWg - 1) : T - 1;
+  const int n_tiles = last / kTile + 1;
+  const int wave_last = t0 + 32 * wave + 31;  // highest row of the wave
 
-  // Q of the wave's rows (B operand: row l32, dims 16 ks + 8 g .. + 7)
+  // Copies of tile j: copy i of this wave is copy number wave + 8 i of the
+  // tile (K copies first, then V).  Rows past T copy row T - 1 (finite
+  // values that the mask gives weight 0).
+  auto issue_tile = [&](int j) __attribute__((always_inline)) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int k0 = j * kTile;
+#pragma unroll
+    for (int i = 0; i < kPerWave; i++) {
+      const int c = wave + kWaves * i;  // wave-uniform
+      if (c < kKCopies) {
+        const int q = 64 * c + ln, r = q / (kKRow / 16), p = q % (kKRow / 16);
+        const int tok = min(k0 + r, T - 1);
+        const uint8_t* src = reinterpret_cast<const uint8_t*>(a.k + ((seq + tok) * H + h) * kDqk);
+        copy16_v(src + ((p ^ ksw(r)) << 4), lds_addr(lds + (j % kNK) * kKBuf + c * 1024));
+      } else {
+        const int cv = c - kKCopies;
+        const int q = 64 * cv + ln, r = q / (kVRow / 16), p = q % (kVRow / 16);
+        const int tok = min(k0 + r, T - 1);
+        const uint8_t* src = reinterpret_cast<const uint8_t*>(a.v + ((seq + tok) * H + h) * kDv);
+        copy16_v(src + ((p ^ sw16(r)) << 4), lds_addr(lds + kVOff + (j % kNV) * kVBuf + cv * 1024));
+      }
+    }
+  };
+
+  // P.V of tile j - 1 runs in step j; before the first tile it runs on a
+  // zeroed V buffer (the one tile -1 maps to) with P = 0.
+  {
+    uint4* z = reinterpret_cast<uint4*>(lds + kVOff + ((kNV - 1) % kNV) * kVBuf);
+    for (int i = tid; i < kVBuf / 16; i += 64 * kWaves) z[i] = uint4{0u, 0u, 0u, 0u};
+  }
+  issue_tile(0);
+  // Q of the wave's rows (B operand: row l32, dims 16 ks + 8 g .. + 7),
+  // taken delivery of here (with tile 0): a wait left to the compiler would
+  // land in the loop and also wait for the copies in flight there
   bf16x8 qf[kDqk / 16];
   {
     const bf16x8* qp = reinterpret_cast<const bf16x8*>(a.q + ((seq + (row_ok ? row : 0)) * H + h) * kDqk + 8 * g);
 #pragma unroll
     for (int ks = 0; ks < kDqk / 16; ks++) qf[ks] = row_ok ? qp[2 * ks] : bf16x8{};
+#pragma unroll
+    for (int ks = 0; ks < kDqk / 16; ks++) asm volatile("" : "+v"(qf[ks]));
   }
+  wait_vm<0>();
+  if (n_tiles > 1) issue_tile(1);
+  __syncthreads();  // tile 0 and the zeroed V buffer are in LDS
+
   f32x16 o[kDv / 32];
 #pragma unroll
   for (int d = 0; d < kDv / 32; d++) o[d] = f32x16{};
   float m_run = kNegInf, l_run = 0.f;
   const float c2 = a.scale * kLog2e;
 
-  const int last = a.causal ? min(T - 1, t0 + kRowsWg - 1) : T - 1;
-  const int n_tiles = last / kTile + 1;
-  const int wave_last = t0 + 32 * wave + 31;  // highest row of the wave
-  // Tile loads: K as 64 tokens x 24 pieces of 8 dims (3 per thread); V as
-  // 16 pieces of 8 dims x 64 tokens, a thread taking two consecutive tokens
-  // of one piece (2 per thread), so that the transposing LDS stores write
-  // both tokens of a dim as one 4-byte word and consecutive lanes hit
-  // consecutive banks.  Tile j + 1 is loaded into registers while tile j is
-  // computed and stored into the other LDS buffer afterwards: one workgroup
-  // barrier per tile.
-  constexpr int kThreads = 64 * kWaves;
-  constexpr int kKPer = kTile * (kDqk / 8) / kThreads, kVPer = 2;
-  static_assert(kTile * (kDv / 8) == kVPer * kThreads, "V tile split");
-  bf16x8 kr[kKPer], vr[kVPer];
-  const int v_tok = 2 * (tid % 32), v_pc = tid / 32;
-  auto load_tile = [&](int k0) {
+  // K operand offsets of this lane: token 32 hf + l32, chunk 2 ks + g at
+  // position (2 ks + g) ^ ksw(token) = 8 (ks >> 2) + ((2 (ks & 3) + g) ^ kx)
+  const int kx = ksw(l32);
+  uint32_t koff[4];
 #pragma unroll
-    for (int i = 0; i < kKPer; i++) {
-      const int p = tid + kThreads * i, tok = p / (kDqk / 8), pc = p % (kDqk / 8);
-      kr[i] = k0 + tok < T ? *reinterpret_cast<const bf16x8*>(a.k + ((seq + k0 + tok) * H + h) * kDqk + 8 * pc)
-                           : bf16x8{};
-    }
-#pragma unroll
-    for (int i = 0; i < kVPer; i++) {
-      const int tok = v_tok + i;
-      vr[i] = k0 + tok < T ? *reinterpret_cast<const bf16x8*>(a.v + ((seq + k0 + tok) * H + h) * kDv + 8 * v_pc)
-                           : bf16x8{};
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < kKPer; i++) {
-      const int p = tid + kThreads * i, tok = p / (kDqk / 8), pc = p % (kDqk / 8);
-      *reinterpret_cast<bf16x8*>(&k_lds2[buf][tok * kKStride + 8 * pc]) = kr[i];
-    }
-#pragma unroll
-    for (int e = 0; e < 8; e++) {
-      bf16x2 w = {vr[0][e], vr[1][e]};
-      *reinterpret_cast<bf16x2*>(&vt_lds2[buf][(8 * v_pc + e) * kVStride + v_tok]) = w;
-    }
-  };
-  // P.V of tile j - 1 runs in step j beside tile j's softmax.  Before the
-  // first tile it runs on a zeroed V buffer with P = 0 (adds nothing), so
-  // the common step has no branch between the two.
+  for (int j = 0; j < 4; j++) koff[j] = (uint32_t)(l32 * kKRow + (((2 * j + g) ^ kx) << 4));
+  // V^T operand reads (transposing): lane loads token 16 kk + row0 (+ 8),
+  // 4 dims of chunk 4 db + w
+  int lnv = lane;
+  asm volatile("" : "+v"(lnv));
+  const int G16v = lnv >> 4, i16v = lnv & 15;
+  const int row0 = 4 * (G16v >> 1) + (i16v >> 2);
+  const int wv = 2 * (G16v & 1) + ((i16v >> 1) & 1);
+  const uint32_t vbase = (uint32_t)(row0 * kVRow + 8 * (i16v & 1));
+  const int vy0 = wv ^ sw16(row0), vy1 = wv ^ sw16(row0 + 8);
+
   bf16x8 pf_prev[kTile / 16];
 #pragma unroll
   for (int kk = 0; kk < kTile / 16; kk++) pf_prev[kk] = bf16x8{};
   float alpha_prev = 1.f;
   bool pend = false;
-  for (int i = tid; i < kDv * kVStride / 2; i += kThreads) reinterpret_cast<unsigned*>(vt_lds2[2])[i] = 0u;
-  auto pv_step = [&](const __bf16* vt) {
+  auto pv_step = [&](int vb_idx) __attribute__((always_inline)) {
+    const uint8_t* vt = lds + kVOff + vb_idx * kVBuf;
 #pragma unroll
     for (int kk = 0; kk < kTile / 16; kk++) {
 #pragma unroll
       for (int d = 0; d < kDv / 32; d++) {
-        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(&vt[(32 * d + l32) * kVStride + 16 * kk + 8 * g]);
-        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf_prev[kk], o[d], 0, 0, 0);
+        const uint8_t* p0 = vt + vbase + (16 * kk) * kVRow + (((4 * d) ^ vy0) << 4);
+        const uint8_t* p1 = vt + vbase + (16 * kk + 8) * kVRow + (((4 * d) ^ vy1) << 4);
+        const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(p0));
+        const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(p1));
+        const bf16x8 vv = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, pf_prev[kk], o[d], 0, 0, 0);
       }
     }
   };
-  auto rescale_prev = [&]() {  // O only needs rescaling when some row's maximum moved
+  auto rescale_prev = [&]() __attribute__((always_inline)) {  // only when some row's maximum moved
     if (__builtin_amdgcn_ballot_w64(alpha_prev != 1.f) != 0) {
 #pragma unroll
       for (int d = 0; d < kDv / 32; d++) o[d] *= alpha_prev;
     }
   };
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-  int cur = 0;  // buffer of tile j; tile j - 1 is in (cur + 2) % 3
+
   for (int j = 0; j < n_tiles; j++) {
     const int k0 = j * kTile;
-    const int prv = cur == 0 ? 2 : cur - 1, nxt = cur == 2 ? 0 : cur + 1;
-    const __bf16* k_lds = k_lds2[cur];
-    const bool more = j + 1 < n_tiles;
-    if (more) load_tile(k0 + kTile);
+    const bool ahead = j + 2 < n_tiles;
+    if (ahead) issue_tile(j + 2);
     if (a.causal && k0 > wave_last) {
       // the whole tile lies above this wave's rows: only finish the last
       // computed tile's P.V (once)
       if (pend) {
         rescale_prev();
-        pv_step(vt_lds2[prv]);
+        pv_step((j + kNV - 1) % kNV);
         pend = false;
       }
     } else {
-
     // S^T[token][row] = K Q^T over 192 dims for the tile's two 32-token
     // halves; lane holds row l32 and tokens 32 hf + 8 (i / 4) + 4 g + i % 4
-    // operand n = 2 ks + hf: token 32 hf + l32, dims 16 ks + 8 g .. + 7
     f32x16 s2[2] = {f32x16{}, f32x16{}};
     {
       constexpr int kN = 2 * (kDqk / 16), kLead = 4, kRing = 6;
-      const uint32_t kb = (uint32_t)reinterpret_cast<uintptr_t>(k_lds);
-      const uint32_t ad[2] = {kb + (uint32_t)((l32 * kKStride + 8 * g) * 2),
-                              kb + (uint32_t)(((32 + l32) * kKStride + 8 * g) * 2)};
+      const uint32_t kb = lds_addr(lds + (j % kNK) * kKBuf);
+      uint32_t ad[4];
+#pragma unroll
+      for (int q = 0; q < 4; q++) ad[q] = kb + koff[q];
       bf16x8 ring[kRing];
+      // operand n = 2 ks + hf
       auto rd = [&](auto NI) {
-        constexpr int n = decltype(NI)::value;
-        lds_rd16<32 * (n / 2)>(ring[n % kRing], ad[n % 2]);
+        constexpr int n = decltype(NI)::value, ks = n / 2, hf = n % 2;
+        lds_rd16<128 * (ks >> 2) + 32 * kKRow * hf>(ring[n % kRing], ad[ks & 3]);
       };
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the counted waits below start from zero
       unroll<kLead>(rd);
       unroll<kN>([&](auto NI) {
         constexpr int n = decltype(NI)::value;
@@ -223,54 +223,37 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) 
     const float muse = m_new == kNegInf ? 0.f : m_new;
     const float alpha = m_run == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m_run - muse);
     m_run = m_new;
-    // P in the operand layout of O^T += V^T P^T without a trip through LDS:
-    // for tokens 16 kk .. 16 kk + 15 lane (l32, g) holds, per half g, 4 of
-    // the 8 tokens its operand needs; swapping the second group of the lower
-    // lanes with the first group of the upper lanes (v_permlane32_swap)
-    // gives every lane its 8 consecutive tokens 16 kk + 8 g .. + 7.
+    // The weights are the P operand as they are: for k-step 2 hf + kk the
+    // transposing V read pairs operand element e with token
+    // 32 hf + 16 kk + 4 g + e (e < 4) or + 4 + e (e >= 4), which is this
+    // lane's score 8 kk + e of the half.
     float psum = 0.f;
     bf16x8 pf[kTile / 16];
 #pragma unroll
     for (int hf = 0; hf < 2; hf++) {
-      float pv[16];
 #pragma unroll
       for (int i = 0; i < 16; i++) {
         // a masked score is -inf, and exp2(-inf) = 0 (muse is finite)
-        pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s2[hf][i], c2, -muse));
-        psum += pv[i];
-      }
-#pragma unroll
-      for (int h2 = 0; h2 < 2; h2++) {  // tokens 32 hf + 16 h2 .. + 15
-        unsigned xw[2], yw[2];
-#pragma unroll
-        for (int e = 0; e < 2; e++) {
-          bf16x2 xa = {(__bf16)pv[8 * h2 + 2 * e], (__bf16)pv[8 * h2 + 2 * e + 1]};
-          bf16x2 ya = {(__bf16)pv[8 * h2 + 4 + 2 * e], (__bf16)pv[8 * h2 + 4 + 2 * e + 1]};
-          const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, xa),
-                                                          __builtin_bit_cast(unsigned, ya), false, false);
-          xw[e] = r[0];
-          yw[e] = r[1];
-        }
-        u32x4 w = {xw[0], xw[1], yw[0], yw[1]};
-        pf[2 * hf + h2] = __builtin_bit_cast(bf16x8, w);
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s2[hf][i], c2, -muse));
+        psum += p;
+        pf[2 * hf + i / 8][i % 8] = (__bf16)p;
       }
     }
     l_run = l_run * alpha + psum;
-    pv_step(vt_lds2[prv]);  // tile j - 1 (or nothing before the first tile)
+    pv_step((j + kNV - 1) % kNV);  // tile j - 1 (or nothing before the first tile)
 #pragma unroll
     for (int kk = 0; kk < kTile / 16; kk++) pf_prev[kk] = pf[kk];
     alpha_prev = alpha;
     pend = true;
     }
-    // tile j + 1 goes to the buffer that tile j - 2 used: last read before
-    // the previous barrier
-    if (more) store_tile(nxt);
+    // tile j + 1 has landed (tile j + 2 may still be in flight)
+    if (ahead) wait_vm<kPerWave>();
+    else wait_vm<0>();
     __syncthreads();
-    cur = nxt;
   }
   if (pend) {
     rescale_prev();
-    pv_step(vt_lds2[cur == 0 ? 2 : cur - 1]);
+    pv_step((n_tiles - 1) % kNV);
   }
 
   // O^T[dim][row]: lane holds row l32, dims 32 d + 8 (i / 4) + 4 g + i % 4
@@ -295,8 +278,11 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) 
 }  // namespace kern
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern::prefill_kernel),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, kern::kLdsBytes);
+  if (e != hipSuccess) return e;
   const dim3 grid((unsigned)((a.T + kern::kRowsWg - 1) / kern::kRowsWg), (unsigned)a.H, (unsigned)a.B);
-  hipLaunchKernelGGL(kern::prefill_kernel, grid, dim3(64 * kern::kWaves), 0, stream, a);
+  hipLaunchKernelGGL(kern::prefill_kernel, grid, dim3(64 * kern::kWaves), kern::kLdsBytes, stream, a);
   return hipGetLastError();
 }
 

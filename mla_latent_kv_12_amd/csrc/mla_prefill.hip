@@ -51,10 +51,16 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) 
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, g = lane >> 5;
-  // the last query tiles see the most keys: dispatch them first
-  const int t0 = (gridDim.x - 1 - blockIdx.x) * kRowsWg;
-  const int h = blockIdx.y, b = blockIdx.z;
   const int T = a.T, H = a.H;
+  // Flat grid, one level of query tiles per H * B workgroups, the last query
+  // tiles (which see the most keys) dispatched first, so that the light
+  // tiles fill in at the end.  Workgroup i runs on XCD i % 8, so with H a
+  // multiple of 8 all query tiles of one head share an XCD and its K/V
+  // tiles meet in that XCD's L2.
+  const int hb_n = H * a.B;
+  const int level = blockIdx.x / hb_n, hb = blockIdx.x - level * hb_n;
+  const int t0 = ((T + kRowsWg - 1) / kRowsWg - 1 - level) * kRowsWg;
+  const int h = hb % H, b = hb / H;
   const size_t seq = (size_t)b * T;
   const int row = t0 + 32 * wave + l32;  // this lane's query position
   const bool row_ok = row < T;
@@ -281,7 +287,7 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern::prefill_kernel),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, kern::kLdsBytes);
   if (e != hipSuccess) return e;
-  const dim3 grid((unsigned)((a.T + kern::kRowsWg - 1) / kern::kRowsWg), (unsigned)a.H, (unsigned)a.B);
+  const dim3 grid((unsigned)((a.T + kern::kRowsWg - 1) / kern::kRowsWg) * (unsigned)a.H * (unsigned)a.B);
   hipLaunchKernelGGL(kern::prefill_kernel, grid, dim3(64 * kern::kWaves), kern::kLdsBytes, stream, a);
   return hipGetLastError();
 }

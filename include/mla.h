@@ -308,8 +308,10 @@ mla_status mla_decode_layer(const void *q_c, const void *w_uk_t, const void *q_r
  * over j <= t when causal != 0, else over all j < T.
  *   q, k  bf16 [B, T, H, 192];  v bf16 [B, T, H, 128]
  *   out   bf16 [B, T, H, 128];  lse fp32 [B, T, H]   (written)
- * softmax_scale finite and > 0.  Limits: B, T >= 1; 1 <= H, B <= 65535.
- * Alignment: q, k, v, out 16 B; lse 4 B.
+ * softmax_scale finite and > 0.  Limits: B, T >= 1; 1 <= H, B <= 65535;
+ * B * T * H <= 2^31 / 192 and (T + 64) * H * 384 <= 2^32 (the kernel's byte
+ * offsets within one sequence are 32-bit).  Alignment: q, k, v, out 16 B;
+ * lse 4 B.
  */
 mla_status mla_prefill(const void *q, const void *k, const void *v, int B, int T, int H,
                        float softmax_scale, int causal, void *out, float *lse, hipStream_t stream);

@@ -514,7 +514,8 @@ mla_status mla_prefill(const void* q, const void* k, const void* v, int B, int T
   if (!q || !k || !v || !out || !lse) return fail(MLA_ERR_NULL, "a required tensor pointer is NULL");
   if (B <= 0 || T <= 0 || H <= 0 || H > 65535 || B > 65535)
     return fail(MLA_ERR_SHAPE, "need B, T >= 1 and 1 <= H, B <= 65535 (got %d, %d, %d)", B, T, H);
-  if ((long long)B * T * H > (1LL << 31) / 192) return fail(MLA_ERR_SHAPE, "B * T * H too large");
+  if ((long long)B * T * H > (1LL << 31) / 192 || (long long)(T + 64) * H * 384 > (1LL << 32))
+    return fail(MLA_ERR_SHAPE, "B * T * H or T * H too large");
   if (!isfinite(softmax_scale) || !(softmax_scale > 0.f))
     return fail(MLA_ERR_SHAPE, "softmax_scale must be finite and > 0");
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(lse, 4))

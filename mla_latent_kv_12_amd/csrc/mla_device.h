@@ -115,6 +115,15 @@ __device__ __forceinline__ void copy16_b(i32x4 rsrc, uint32_t voff, uint32_t lds
       :
       : "v"(voff), "s"(rsrc), "{m0}"(lds));
 }
+// The same with a wave-uniform byte offset added to every lane's (the range
+// check applies to the sum).
+__device__ __forceinline__ void copy16_bs(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile(
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %0, %1, %2 offen lds"
+      :
+      : "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds));
+}
 // Raw buffer resource over `bytes` bytes from `base` (gfx9 word 3: untyped
 // 32-bit data, no swizzle); every word is wave-uniform.
 __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {

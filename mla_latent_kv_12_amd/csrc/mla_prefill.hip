@@ -69,27 +69,36 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) 
   const int wave_last = t0 + 32 * wave + 31;  // highest row of the wave
 
   // Copies of tile j: copy i of this wave is copy number wave + 8 i of the
-  // tile (K copies first, then V).  Rows past T copy row T - 1 (finite
-  // values that the mask gives weight 0).
+  // tile, K copies (i < 3) first, then V.  They go through buffer resources
+  // over this (sequence, head)'s rows, so a row past T reads zeros (the
+  // hardware range check; the mask gives those tokens weight 0), and each
+  // lane's offset within a tile is computed once: a tile adds one
+  // wave-uniform offset.
+  static_assert(kKCopies == 3 * kWaves && kVCopies == 2 * kWaves, "copy split");
+  const uint32_t krow_b = (uint32_t)H * kKRow, vrow_b = (uint32_t)H * kDv * 2;
+  const i32x4 krs = make_rsrc(a.k + (seq * H + h) * kDqk, (uint32_t)(T - 1) * krow_b + kKRow);
+  const i32x4 vrs = make_rsrc(a.v + (seq * H + h) * kDv, (uint32_t)(T - 1) * vrow_b + kVRow);
+  uint32_t coff[kPerWave];
+#pragma unroll
+  for (int i = 0; i < kPerWave; i++) {
+    int c = wave + kWaves * i;
+    if (i < 3) {
+      const int q = 64 * c + lane, r = q / (kKRow / 16), p = q % (kKRow / 16);
+      coff[i] = (uint32_t)r * krow_b + (uint32_t)((p ^ ksw(r)) << 4);
+    } else {
+      c -= kKCopies;
+      const int q = 64 * c + lane, r = q / (kVRow / 16), p = q % (kVRow / 16);
+      coff[i] = (uint32_t)r * vrow_b + (uint32_t)((p ^ sw16(r)) << 4);
+    }
+  }
+  const uint32_t lds_wave = __builtin_amdgcn_readfirstlane(lds_addr(lds) + 1024 * wave);
   auto issue_tile = [&](int j) __attribute__((always_inline)) {
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
-    const int k0 = j * kTile;
+    const uint32_t k0 = (uint32_t)(j * kTile);
+    const uint32_t kd = lds_wave + (j % kNK) * kKBuf, vd = lds_wave + kVOff + (j % kNV) * kVBuf;
 #pragma unroll
     for (int i = 0; i < kPerWave; i++) {
-      const int c = wave + kWaves * i;  // wave-uniform
-      if (c < kKCopies) {
-        const int q = 64 * c + ln, r = q / (kKRow / 16), p = q % (kKRow / 16);
-        const int tok = min(k0 + r, T - 1);
-        const uint8_t* src = reinterpret_cast<const uint8_t*>(a.k + ((seq + tok) * H + h) * kDqk);
-        copy16_v(src + ((p ^ ksw(r)) << 4), lds_addr(lds + (j % kNK) * kKBuf + c * 1024));
-      } else {
-        const int cv = c - kKCopies;
-        const int q = 64 * cv + ln, r = q / (kVRow / 16), p = q % (kVRow / 16);
-        const int tok = min(k0 + r, T - 1);
-        const uint8_t* src = reinterpret_cast<const uint8_t*>(a.v + ((seq + tok) * H + h) * kDv);
-        copy16_v(src + ((p ^ sw16(r)) << 4), lds_addr(lds + kVOff + (j % kNV) * kVBuf + cv * 1024));
-      }
+      if (i < 3) copy16_bs(krs, coff[i], k0 * krow_b, kd + i * kWaves * 1024);
+      else copy16_bs(vrs, coff[i], k0 * vrow_b, vd + (i - 3) * kWaves * 1024);
     }
   };
 

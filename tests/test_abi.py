@@ -176,6 +176,8 @@ def test_projections_reject_before_launch(fn, args, code):
     ((FAKE, FAKE, FAKE, 1, 64, 0, 0.1, 1, FAKE, FAKE), SHAPE),
     ((FAKE, FAKE, FAKE, 1, 64, 8, 0.0, 1, FAKE, FAKE), SHAPE),
     ((FAKE, FAKE, FAKE, 1, 64, 8, float("nan"), 1, FAKE, FAKE), SHAPE),
+    ((FAKE, FAKE, FAKE, 2, 65536, 128, 0.1, 1, FAKE, FAKE), SHAPE),   # B * T * H
+    ((FAKE, FAKE, FAKE, 1, 87371, 128, 0.1, 1, FAKE, FAKE), SHAPE),   # (T + 64) * H * 384 > 2^32
     ((FAKE + 8, FAKE, FAKE, 1, 64, 8, 0.1, 1, FAKE, FAKE), ALIGN),
     ((FAKE, FAKE, FAKE, 1, 64, 8, 0.1, 1, FAKE, FAKE + 2), ALIGN),
 ])

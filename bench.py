@@ -183,6 +183,7 @@ def bench_append(args):
     sc = inp["kv_scales"].to(dev) if fp8 else None
     bt, L = inp["block_table"].to(dev), inp["cache_seqlens"].to(dev)
     new = S._randn_bf16((B, Sq, 576), torch.Generator().manual_seed(99)).to(dev)
+    settle(lambda _: mla.kv_append(new, kv, bt, L, kv_scales=sc), args.settle_s)
     for _ in range(args.warmup):
         mla.kv_append(new, kv, bt, L, kv_scales=sc)
     torch.cuda.synchronize()
@@ -227,6 +228,7 @@ def bench_select(args):
     scores = torch.randn((B, Sq, nbk), generator=torch.Generator().manual_seed(98)).to(dev)
     n_sel = topk // 64
     idx = torch.empty((B, Sq, topk), dtype=torch.int32, device=dev)
+    settle(lambda _: mla.dsa_select(scores, L, n_select=n_sel, indices=idx), args.settle_s)
     for _ in range(args.warmup):
         mla.dsa_select(scores, L, n_select=n_sel, indices=idx)
     torch.cuda.synchronize()
@@ -271,6 +273,7 @@ def bench_proj(args):
     w = (torch.randn((H, kout, kin), generator=gen) * 512 ** -0.5).to(torch.bfloat16).to(dev)
     out = torch.empty((M, H, kout), dtype=torch.bfloat16, device=dev)
     f = mla.absorb_query if absorb else mla.project_out
+    settle(lambda _: f(x, w, out=out), args.settle_s)
     for _ in range(args.warmup):
         f(x, w, out=out)
     torch.cuda.synchronize()
@@ -413,6 +416,7 @@ def bench_prefill(args):
     out = torch.empty((B, T, H, 128), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((B, T, H), dtype=torch.float32, device=dev)
     scale = 1.0 / np.sqrt(192.0)
+    settle(lambda _: mla.prefill(q, k, v, scale, out=out, lse=lse), args.settle_s)
     for _ in range(args.warmup):
         mla.prefill(q, k, v, scale, out=out, lse=lse)
     torch.cuda.synchronize()

@@ -92,14 +92,16 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) 
     }
   }
   const uint32_t lds_wave = __builtin_amdgcn_readfirstlane(lds_addr(lds) + 1024 * wave);
-  auto issue_tile = [&](int j) __attribute__((always_inline)) {
+  auto issue_copy = [&](int j, auto I) __attribute__((always_inline)) {
+    constexpr int i = decltype(I)::value;
     const uint32_t k0 = (uint32_t)(j * kTile);
-    const uint32_t kd = lds_wave + (j % kNK) * kKBuf, vd = lds_wave + kVOff + (j % kNV) * kVBuf;
-#pragma unroll
-    for (int i = 0; i < kPerWave; i++) {
-      if (i < 3) copy16_bs(krs, coff[i], k0 * krow_b, kd + i * kWaves * 1024);
-      else copy16_bs(vrs, coff[i], k0 * vrow_b, vd + (i - 3) * kWaves * 1024);
-    }
+    if constexpr (i < 3)
+      copy16_bs(krs, coff[i], k0 * krow_b, lds_wave + (j % kNK) * kKBuf + i * kWaves * 1024);
+    else
+      copy16_bs(vrs, coff[i], k0 * vrow_b, lds_wave + kVOff + (j % kNV) * kVBuf + (i - 3) * kWaves * 1024);
+  };
+  auto issue_tile = [&](int j) __attribute__((always_inline)) {
+    unroll<kPerWave>([&](auto I) { issue_copy(j, I); });
   };
 
   // P.V of tile j - 1 runs in step j; before the first tile it runs on a
@@ -176,8 +178,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) 
   for (int j = 0; j < n_tiles; j++) {
     const int k0 = j * kTile;
     const bool ahead = j + 2 < n_tiles;
-    if (ahead) issue_tile(j + 2);
     if (a.causal && k0 > wave_last) {
+      if (ahead) issue_tile(j + 2);
       // the whole tile lies above this wave's rows: only finish the last
       // computed tile's P.V (once)
       if (pend) {
@@ -187,7 +189,9 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) 
       }
     } else {
     // S^T[token][row] = K Q^T over 192 dims for the tile's two 32-token
-    // halves; lane holds row l32 and tokens 32 hf + 8 (i / 4) + 4 g + i % 4
+    // halves; lane holds row l32 and tokens 32 hf + 8 (i / 4) + 4 g + i % 4.
+    // Tile j + 2's copies go out between the MFMAs (a copy issued right
+    // after another stalls its wave far longer than one between MFMAs).
     f32x16 s2[2] = {f32x16{}, f32x16{}};
     {
       constexpr int kN = 2 * (kDqk / 16), kLead = 4, kRing = 6;
@@ -207,6 +211,9 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) 
         constexpr int n = decltype(NI)::value;
         lds_ready<(kLead - 1 < kN - 1 - n ? kLead - 1 : kN - 1 - n)>(ring[n % kRing]);
         s2[n % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[n % kRing], qf[n / 2], s2[n % 2], 0, 0, 0);
+        if constexpr (n % 5 == 2 && n / 5 < kPerWave) {
+          if (ahead) issue_copy(j + 2, std::integral_constant<int, n / 5>{});
+        }
         if constexpr (n + kLead < kN) rd(std::integral_constant<int, n + kLead>{});
       });
     }
@@ -234,10 +241,15 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillArgs a) 
       }
     }
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    const float m_new = fmaxf(m_run, mloc * c2);
-    const float muse = m_new == kNegInf ? 0.f : m_new;
-    const float alpha = m_run == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m_run - muse);
-    m_run = m_new;
+    // The running maximum moves only when the tile exceeds it by more than
+    // kRescaleSlack (log2 units), so O is rarely rescaled; weights stay
+    // below 2^kRescaleSlack.  Before the row's first visible token O and l
+    // are zero and need no factor.
+    const float mc = mloc * c2;
+    const bool need = mc > m_run + kRescaleSlack;  // -inf + slack = -inf
+    const float alpha = need && m_run != kNegInf ? __builtin_amdgcn_exp2f(m_run - mc) : 1.f;
+    if (need) m_run = mc;
+    const float muse = m_run == kNegInf ? 0.f : m_run;
     // The weights are the P operand as they are: for k-step 2 hf + kk the
     // transposing V read pairs operand element e with token
     // 32 hf + 16 kk + 4 g + e (e < 4) or + 4 + e (e >= 4), which is this

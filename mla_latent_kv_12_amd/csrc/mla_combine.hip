@@ -70,12 +70,17 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
     f16x8 v[kBatch];
 #pragma unroll
     for (int k = 0; k < kBatch; k++) {
-      // past the last split: reload the last one with weight 0
-      const int s = min(i0 + k, ns - 1);
-      const size_t sp = (size_t)(base + s);
-      ls[k] = *reinterpret_cast<const float2*>(plse + sp * a.split_rows);
-      sc[k] = *reinterpret_cast<const float2*>(psc + sp * a.split_rows);
-      v[k] = *reinterpret_cast<const f16x8*>(po + sp * split_elems);
+      // ns is the same for the whole block: past the last split no load
+      if (i0 + k < ns) {
+        const size_t sp = (size_t)(base + i0 + k);
+        ls[k] = *reinterpret_cast<const float2*>(plse + sp * a.split_rows);
+        sc[k] = *reinterpret_cast<const float2*>(psc + sp * a.split_rows);
+        v[k] = *reinterpret_cast<const f16x8*>(po + sp * split_elems);
+      } else {
+        ls[k] = float2{kNegInf, kNegInf};
+        sc[k] = float2{0.f, 0.f};
+        v[k] = f16x8{};
+      }
     }
     float bm0 = mx0, bm1 = mx1;
 #pragma unroll

@@ -553,47 +553,63 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_sparse_hg(DecodeArgs a) {
   if (w == 0 && lane < 32) a.ws_plse[part * 32 + r] = lse2;
 }
 
-// Merge of the ranges of every item, in range order: thread t of the item's
-// 4096 handles the four values t of the partials (fragment order: t >> 10 =
-// the wave that stored them, t >> 8 = dim block, (t >> 6) & 3 = 8-dim group,
-// t & 63 = lane), i.e. row t & 31 and dims
-// 32 (t >> 8) + 8 ((t >> 6) & 3) + 4 ((t >> 5) & 1) .. +3.
+// Merge of the ranges of every item, in range order.  A partial holds 4096
+// pieces of four values in fragment order (piece t: t >> 10 = the wave that
+// stored it, lane t & 63), i.e. row t & 31 and dims
+// 32 (t >> 8) + 8 ((t >> 6) & 3) + 4 ((t >> 5) & 1) .. +3.  Thread u of the
+// item's 2048 takes pieces 2u and 2u + 1, 16 contiguous bytes: rows r0 and
+// r0 + 1 at the same four dims.
 __global__ __launch_bounds__(256) void combine_hg(DecodeArgs a) {
   const int item = blockIdx.x;
-  const int t = blockIdx.y * 256 + threadIdx.x;
+  const int t0 = 2 * (blockIdx.y * 256 + threadIdx.x);
   const int NR = a.hg_groups, S = a.hg_splits;
   const int hg = item % NR, su = item / NR;
   const int rows = min(32, a.H - 32 * hg);
-  const int r = t & 31;
-  if (r >= rows) return;
-  const size_t row = (size_t)su * a.H + 32 * hg + r;
-  const int d = 32 * (t >> 8) + 8 * ((t >> 6) & 3) + 4 * ((t >> 5) & 1);
+  const int r0 = t0 & 31;
+  if (r0 >= rows) return;
+  const bool second = r0 + 1 < rows;
+  const size_t row0 = (size_t)su * a.H + 32 * hg + r0;
+  const int d = 32 * (t0 >> 8) + 8 * ((t0 >> 6) & 3) + 4 * ((t0 >> 5) & 1);
+  const int qw = t0 >> 10;  // the quarter of the dims (the wave that stored it)
   const size_t base = (size_t)item * S;
-  float mx = kNegInf;
-  for (int s = 0; s < S; s++) mx = fmaxf(mx, a.ws_plse[(base + s) * 32 + r]);
-  uint16_t* dst = a.out + row * kDC + d;
-  const bool lse_writer = t < 32;
-  if (mx == kNegInf) {
-    *reinterpret_cast<u32x2*>(dst) = u32x2{0u, 0u};
-    if (lse_writer) a.lse[row] = kNegInf;
-    return;
-  }
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  float wsum = 0.f;
-  const _Float16* const po = reinterpret_cast<const _Float16*>(a.ws_po);
-  const int qw = t >> 10;  // the quarter of the dims (the wave that stored it)
+  const _Float16* const po = reinterpret_cast<const _Float16*>(a.ws_po) + 4 * t0;
+  float mx0 = kNegInf, mx1 = kNegInf;
   for (int s = 0; s < S; s++) {
-    const float ws = __builtin_amdgcn_exp2f(a.ws_plse[(base + s) * 32 + r] - mx);  // 0: empty range
-    const f16x4 h = *reinterpret_cast<const f16x4*>(po + (base + s) * (16 * 1024) + 4 * t);
-    const float f = ws * a.ws_psc[(base + s) * 128 + qw * 32 + r];
-    acc += f * f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
-    wsum += ws;
+    const float2 l = *reinterpret_cast<const float2*>(a.ws_plse + (base + s) * 32 + r0);
+    mx0 = fmaxf(mx0, l.x);
+    mx1 = fmaxf(mx1, l.y);
   }
-  const float inv = 1.0f / wsum;
-  bf16x2 p0 = {(__bf16)(acc[0] * inv), (__bf16)(acc[1] * inv)};
-  bf16x2 p1 = {(__bf16)(acc[2] * inv), (__bf16)(acc[3] * inv)};
-  *reinterpret_cast<u32x2*>(dst) = u32x2{__builtin_bit_cast(unsigned, p0), __builtin_bit_cast(unsigned, p1)};
-  if (lse_writer) a.lse[row] = (mx + __log2f(wsum)) * kLn2;
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  float ws0 = 0.f, ws1 = 0.f;
+  for (int s = 0; s < S; s++) {
+    const float2 l = *reinterpret_cast<const float2*>(a.ws_plse + (base + s) * 32 + r0);
+    const float2 sc = *reinterpret_cast<const float2*>(a.ws_psc + (base + s) * 128 + qw * 32 + r0);
+    const f16x8 h = *reinterpret_cast<const f16x8*>(po + (base + s) * (16 * 1024));
+    // weight 0 for an empty range (lse -inf) and for a row with no token
+    const float w0 = mx0 == kNegInf ? 0.f : __builtin_amdgcn_exp2f(l.x - mx0);
+    const float w1 = mx1 == kNegInf ? 0.f : __builtin_amdgcn_exp2f(l.y - mx1);
+    ws0 += w0;
+    ws1 += w1;
+    const float f0 = w0 * sc.x, f1 = w1 * sc.y;
+    acc0 += f0 * f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+    acc1 += f1 * f32x4{(float)h[4], (float)h[5], (float)h[6], (float)h[7]};
+  }
+  const bool lse_writer = t0 < 32;
+  auto put = [&](size_t row, const f32x4& acc, float wsum, float mx) {
+    uint16_t* dst = a.out + row * kDC + d;
+    if (mx == kNegInf) {
+      *reinterpret_cast<u32x2*>(dst) = u32x2{0u, 0u};
+      if (lse_writer) a.lse[row] = kNegInf;
+      return;
+    }
+    const float inv = 1.0f / wsum;
+    const bf16x2 p0 = {(__bf16)(acc[0] * inv), (__bf16)(acc[1] * inv)};
+    const bf16x2 p1 = {(__bf16)(acc[2] * inv), (__bf16)(acc[3] * inv)};
+    *reinterpret_cast<u32x2*>(dst) = u32x2{__builtin_bit_cast(unsigned, p0), __builtin_bit_cast(unsigned, p1)};
+    if (lse_writer) a.lse[row] = (mx + __log2f(wsum)) * kLn2;
+  };
+  put(row0, acc0, ws0, mx0);
+  if (second) put(row0 + 1, acc1, ws1, mx1);
 }
 
 }  // namespace kern
@@ -608,7 +624,7 @@ hipError_t launch_sparse_hg(const Geometry& g, const DecodeArgs& a, hipStream_t 
   hipLaunchKernelGGL(decode_bf16_sparse_hg, dim3((unsigned)grid), dim3(256), Hg::kLdsBytes, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess || g.hg_splits == 1) return e;
-  hipLaunchKernelGGL(kern::combine_hg, dim3((unsigned)(g.n_su * g.hg_groups), 16), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(kern::combine_hg, dim3((unsigned)(g.n_su * g.hg_groups), 8), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

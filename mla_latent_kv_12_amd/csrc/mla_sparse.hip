@@ -198,28 +198,8 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_sparse_hg(DecodeArgs a) {
     }
   };
 
-  // Round 0 lookups.  The block-table row is fetched towards L2 beside the
-  // index loads (into a scratch area of LDS), so the dependent page lookups
-  // find it there.  Issue order: index entries, then their pages (vector
-  // loads retire in order); the empty asm statements with a memory clobber
-  // keep the compiler from reordering the groups.
-  const int ea = e_lo + lane, eb = ea + 64;
-  int va = -1, vb = -1, pa = -1, pbg = -1;
-  if (nch > 0) {
-    const int nb = min(a.bt_stride, 1024);  // entries: up to 4 KB per row
-#pragma unroll
-    for (int k = 0; k < 4; k++) {
-      const int e = 256 * k + 64 * w + lane;
-      if (e < nb) copy4_v(bt_row + e, lds_addr(lds + Y::kLookOff + w * 1024 + k * 256));
-    }
-    va = idx_row[min(ea, e_hi - 1)];
-    vb = idx_row[min(eb, e_hi - 1)];
-    asm volatile("" ::: "memory");
-    pa = bt_row[min(max(va >> 6, 0), a.bt_stride - 1)];
-    pbg = bt_row[min(max(vb >> 6, 0), a.bt_stride - 1)];
-    asm volatile("" ::: "memory");
-  }
-  // The group's 32 query rows, once per workgroup: 36 direct copies of whole
+  // The group's 32 query rows, once per workgroup, issued first so that their
+  // round trip overlaps the index and page lookups': 36 direct copies of whole
   // rows (9 per wave) into slot 1 of waves 0 (rows 0..15) and 1 (rows
   // 16..31), in the layout of a chunk, so that every wave reads its score
   // operand out of LDS as it reads the cache rows.  Rows past the head count
@@ -245,6 +225,27 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_sparse_hg(DecodeArgs a) {
     }
   }
   asm volatile("" ::: "memory");
+  // Round 0 lookups.  The block-table row is fetched towards L2 beside the
+  // index loads (into a scratch area of LDS), so the dependent page lookups
+  // find it there.  Issue order: index entries, then their pages (vector
+  // loads retire in order); the empty asm statements with a memory clobber
+  // keep the compiler from reordering the groups.
+  const int ea = e_lo + lane, eb = ea + 64;
+  int va = -1, vb = -1, pa = -1, pbg = -1;
+  if (nch > 0) {
+    const int nb = min(a.bt_stride, 1024);  // entries: up to 4 KB per row
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      const int e = 256 * k + 64 * w + lane;
+      if (e < nb) copy4_v(bt_row + e, lds_addr(lds + Y::kLookOff + w * 1024 + k * 256));
+    }
+    va = idx_row[min(ea, e_hi - 1)];
+    vb = idx_row[min(eb, e_hi - 1)];
+    asm volatile("" ::: "memory");
+    pa = bt_row[min(max(va >> 6, 0), a.bt_stride - 1)];
+    pbg = bt_row[min(max(vb >> 6, 0), a.bt_stride - 1)];
+    asm volatile("" ::: "memory");
+  }
   if (nch > 0) {
     const int i0 = ea < e_hi ? va : -1, i1 = eb < e_hi ? vb : -1;
     t0 = tok_of(i0, pa);

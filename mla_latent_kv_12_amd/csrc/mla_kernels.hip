@@ -803,6 +803,7 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
   // one in flight.
   constexpr int kQ = W::kLeadDma + 2;
   DD fq[kQ];
+  UnitInfo ui{};
   if constexpr (SPARSE) {
 #pragma unroll 1
     for (int x = 0; x < W::kLeadCur; x++) {
@@ -828,8 +829,18 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
       fq[i] = cursor_desc();
       next();
     }
+    // Every workgroup starts at once, so the first requests queue behind the
+    // whole opening burst: the first unit's Q goes out right after item 0's
+    // copies and before the later items', and is taken before those are
+    // issued, so that item 0 and Q lead the burst.
+    copy_all(0, source_dense(fq[0]));
+    if (fq[0].u >= 0) {
+      ui = unit_info(a, false, fq[0].u);
+      load_q(ui);
+      take_q();
+    }
 #pragma unroll
-    for (int z = 0; z < W::kLeadDma; z++) copy_all(z, source_dense(fq[z]));
+    for (int z = 1; z < W::kLeadDma; z++) copy_all(z, source_dense(fq[z]));
   }
 
   // ------------------------------------------------------------ main loop
@@ -848,11 +859,12 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
     dc.u = fq[0].u;
   }
   int uu = dc.u;
-  UnitInfo ui{};
-  if (uu >= 0) {
-    ui = unit_info(a, SPARSE, uu);
-    load_q(ui);
-    take_q();
+  if constexpr (SPARSE) {
+    if (uu >= 0) {
+      ui = unit_info(a, SPARSE, uu);
+      load_q(ui);
+      take_q();
+    }
   }
   // Set-up of item s at the top of its step: where the copies of item
   // s + kLeadDma come from, and (dense) the rows item s shows.

@@ -272,9 +272,10 @@ mla_status mla_project_out(const void *out_latent, const void *w_uv, void *o, in
  * The whole absorbed decode layer for a dense (non-sparse) cache ("MLA 最佳
  * 算子全景调研" §2: the gain of a fused decode comes from doing absorption,
  * attention and output projection together), in four launches: the query
- * absorption with the split-KV schedule as one more workgroup of it (so the
- * main pass reads its share instead of computing it), the main pass, the
- * split merge and the output projection.  Equivalent to
+ * absorption, the main pass (which schedules itself up to 2048 units;
+ * beyond, the split-KV schedule runs as one more workgroup of the
+ * absorption launch and the main pass reads it), the split merge and the
+ * output projection.  Equivalent to
  * mla_absorb_query, then mla_decode on its q_nope, then mla_project_out on
  * the decode's out, with the same bf16 roundings of q_nope and of the
  * latent output between the steps.

@@ -402,7 +402,15 @@ mla_status mla_decode_layer(const void* q_c, const void* w_uk_t, const void* q_r
   pj.c = static_cast<uint16_t*>(o);
   pj.M = B * Sq;
   pj.H = H;
-  hipError_t e = mla::launch_absorb_plan(la, stream);
+  // Up to kFoldUnits units the main pass schedules itself and the absorption
+  // is the plain GEMM; beyond, the schedule rides in the absorption launch.
+  hipError_t e;
+  if (g.n_units <= mla::kFoldUnits) {
+    la.d.fold_plan = 1;
+    e = mla::launch_proj(la.pa, true, stream);
+  } else {
+    e = mla::launch_absorb_plan(la, stream);
+  }
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "absorb launch: %s", hipGetErrorString(e));
   e = mla::launch_decode(g, la.d, kv_dtype == MLA_KV_FP8_E4M3, stream);
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));

@@ -117,7 +117,10 @@ def test_layer_full_size_against_the_oracle_chain_and_unfused():
                          [("bf16", False, 3, 1, 128, (700, 65, 1), 0),
                           ("fp8", True, 3, 2, 20, (333, 130, 2), 0),
                           ("bf16", True, 2, 3, 64, (500, 9), 7),
-                          ("bf16", False, 5, 1, 128, (0, 300, 1200, 64, 700), 300)])
+                          ("bf16", False, 5, 1, 128, (0, 300, 1200, 64, 700), 300),
+                          # more units than the main pass schedules itself: the
+                          # schedule runs in the absorption launch
+                          ("bf16", False, 2100, 1, 16, tuple((37 * i) % 150 for i in range(2100)), 0)])
 def test_layer_shapes(kv, causal, B, Sq, H, lens, num_wg):
     cfg = dict(B=B, Sq=Sq, H=H, lens=("list", lens), kv=kv, shuffle=True, causal=causal, topk=0,
                name=f"layer {kv} B{B} Sq{Sq} H{H}")

@@ -20,12 +20,12 @@ constexpr int kBytesFp8Row = kD;        // 576
 constexpr int kTileBf16 = kPage * kBytesBf16Row;  // 73728
 constexpr int kTileFp8 = kPage * kBytesFp8Row;    // 36864
 
-// Scheduling constants: a split costs this many tiles of fixed work (its
-// query load and its partial written and read back: ~660 KB at 128 rows,
-// nine 72 KB tiles' worth of bytes; 6 measured best), and a workgroup is
-// never given less work.
-constexpr int kSplitCost = 6;
-constexpr int kMinWgCost = 2;
+// Scheduling constants, in 32-token chunks (the unit of work of the main
+// pass): a split costs this many chunks of fixed work (its query load, its
+// first chunk without the pipeline, its partial written and read back; 8
+// measured best of 5 to 12), and a workgroup is never given less work.
+constexpr int kSplitCost = 8;
+constexpr int kMinWgCost = 4;
 // Decodes of up to this many units schedule themselves inside the main pass
 // (its LDS holds the cost prefix); larger ones get a scheduling launch.
 constexpr int kFoldUnits = 2048;

@@ -161,8 +161,9 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
 
   // ------------------------------------------------------------ cursor
   // The lookup cursor walks the workgroup's chunks: unit cu (-1 once done),
-  // tile ct, half ch, tile range end chi, sequence (dense b / sparse su) cs
-  // and its length cL.  Every wave runs it (uniform scalar code).
+  // chunk cc (tile cc / 2, half cc % 2), chunk range end chi, sequence
+  // (dense b / sparse su) cs and its length cL.  Every wave runs it (uniform
+  // scalar code).
   // This workgroup's share of the schedule: computed here (the LDS ring is
   // still free) unless a scheduling launch already wrote it.
   WgSched sc;
@@ -179,37 +180,29 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
     sc.b0 = ldc(a.ws_meta + 4 * uc + 1);
   }
   const int u_end = sc.u1, t_end = sc.t1;
-  int cu = sc.u0, ct = sc.t0, ch = 0, chi = 0, cs = 0, cL = 0;
-  auto enter = [&]() {  // settle (cu, ct) on the next unit with a chunk left
+  int cu = sc.u0, cc = sc.t0, chi = 0, cs = 0, cL = 0;
+  auto enter = [&]() {  // settle (cu, cc) on the next unit with a chunk left
     for (;;) {
       if (cu > u_end || cu >= a.n_units) {
         cu = -1;
         return;
       }
-      chi = (cu == u_end) ? t_end : unit_tiles(a, SPARSE, cu);
-      if (ct < chi) break;
+      chi = (cu == u_end) ? t_end : unit_chunks(a, SPARSE, cu);
+      if (cc < chi) break;
       cu++;
-      ct = 0;
+      cc = 0;
     }
-    ch = 0;
     cs = cu / a.row_blocks;
     const int b = SPARSE ? cs / a.Sq : cs;
     cL = max(ldc(a.seqlens + b), 0);
   };
   auto next = [&]() {
     if (cu < 0) return;
-    const int span = SPARSE ? a.topk : cL;   // entries (tokens) of the unit
-    if (ch == 0 && kPage * ct + 32 < span) {
-      ch = 1;
-      return;
-    }
-    ct++;
-    if (ct >= chi) {
+    cc++;
+    if (cc >= chi) {
       cu++;
-      ct = 0;
+      cc = 0;
       enter();
-    } else {
-      ch = 0;
     }
   };
   enter();
@@ -224,7 +217,8 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
   auto cursor_desc = [&]() -> DD {
     DD d;
     d.u = cu;
-    d.remh = 2 * (cL - 32 * (2 * ct + ch)) + ch;
+    const int ct = cc >> 1;
+    d.remh = 2 * (cL - 32 * cc) + (cc & 1);
     d.pg = (cu >= 0 && ct < a.bt_stride) ? ldc(a.block_table + (size_t)cs * a.bt_stride + ct) : -1;
     return d;
   };
@@ -240,7 +234,7 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
   auto lookup = [&](int x) {
     if (rg != 0) return;
     int* d = desc(x);
-    const int th = cu >= 0 ? 2 * ct + ch : -1;
+    const int th = cu >= 0 ? cc : -1;
     if constexpr (SPARSE) {
       const int b = cs / a.Sq;
       if (lane == 0) {
@@ -249,7 +243,7 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
         d[2] = b;
         d[3] = cL;
       }
-      const int e = kPage * ct + 32 * ch + lane;
+      const int e = 32 * cc + lane;
       const bool ok = cu >= 0 && lane < 32 && e < a.topk;
       const bool any = __builtin_amdgcn_ballot_w64(ok) != 0;
       int* ring = idx_ring + (x & (W::kRing - 1)) * 32;
@@ -708,14 +702,14 @@ __device__ __forceinline__ void decode_wide(const DecodeArgs& a) {
     wait_lds();
     barrier();
     for (; eu < uu; eu++) {
-      const int n = unit_tiles(a, SPARSE, eu);
+      const int n = unit_chunks(a, SPARSE, eu);
       int ns, gf;
       unit_splits(eC, n, sc.q, &ns, &gf);
       eC += n + kSplitCost;
       eB += ns;
     }
     int n_splits, gfirst;
-    unit_splits(eC, unit_tiles(a, SPARSE, uu), sc.q, &n_splits, &gfirst);
+    unit_splits(eC, unit_chunks(a, SPARSE, uu), sc.q, &n_splits, &gfirst);
     const int split = eB + (wg - gfirst);
 #pragma unroll
     for (int rb = 0; rb < R; rb++) {

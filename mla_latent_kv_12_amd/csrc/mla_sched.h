@@ -1,6 +1,6 @@
 // Split-KV scheduling shared by the decode kernels of libmla: the units a
-// decode is folded into, and the pass that partitions their 64-token tiles
-// over the persistent workgroups.
+// decode is folded into, and the pass that partitions their 32-token chunks
+// (half pages) over the persistent workgroups.
 #pragma once
 
 #include "mla_device.h"
@@ -9,11 +9,11 @@
 namespace mla {
 namespace kern {
 
-__device__ __forceinline__ int unit_tiles(const DecodeArgs& a, bool sparse, int u) {
-  if (sparse) return (a.topk + kPage - 1) / kPage;
+__device__ __forceinline__ int unit_chunks(const DecodeArgs& a, bool sparse, int u) {
+  if (sparse) return (a.topk + 31) / 32;
   int su = u / a.row_blocks;
   int L = ldc(a.seqlens + su);
-  return L > 0 ? (L + kPage - 1) / kPage : 0;
+  return L > 0 ? (L + 31) / 32 : 0;
 }
 
 struct UnitInfo {
@@ -35,9 +35,9 @@ __device__ __forceinline__ UnitInfo unit_info(const DecodeArgs& a, bool sparse, 
 }
 
 // ---------------------------------------------------------------------------
-// Scheduler.  Cost of unit u = its tiles + kSplitCost.  Workgroup g owns the
-// cost interval [g*Q, (g+1)*Q) with Q = max(ceil(total / G), kMinWgCost); a
-// tile belongs to the workgroup whose interval holds its cost position.
+// Scheduler.  Cost of unit u = its chunks + kSplitCost.  Workgroup g owns
+// the cost interval [g*Q, (g+1)*Q) with Q = max(ceil(total / G), kMinWgCost);
+// a chunk belongs to the workgroup whose interval holds its cost position.
 // ---------------------------------------------------------------------------
 // Units whose cost prefix fits here are searched in LDS (a binary search in
 // global memory costs one memory round trip per level).
@@ -57,7 +57,7 @@ __device__ __forceinline__ void plan_work(const DecodeArgs& a) {
   const int lo = min(U, tid * per), hi = min(U, lo + per);
 
   int s = 0;
-  for (int u = lo; u < hi; u++) s += unit_tiles(a, SPARSE, u) + kSplitCost;
+  for (int u = lo; u < hi; u++) s += unit_chunks(a, SPARSE, u) + kSplitCost;
   part[tid] = s;
   __syncthreads();
   for (int off = 1; off < 256; off <<= 1) {
@@ -70,7 +70,7 @@ __device__ __forceinline__ void plan_work(const DecodeArgs& a) {
   for (int u = lo; u < hi; u++) {
     C[u] = run;
     if (in_lds) c_lds[u] = run;
-    run += unit_tiles(a, SPARSE, u) + kSplitCost;
+    run += unit_chunks(a, SPARSE, u) + kSplitCost;
   }
   const int total = part[255];
   if (tid == 0) {
@@ -139,7 +139,7 @@ __device__ __forceinline__ void plan_work(const DecodeArgs& a) {
 }
 
 // What one workgroup of the main pass needs of the schedule: its first and
-// last (unit, tile) -- [u0, t0) up to (u1, t1), tiles of u1 below t1 -- the
+// last (unit, chunk) -- [u0, t0) up to (u1, t1), chunks of u1 below t1 -- the
 // cost quantum q, and the cost prefix c0 and split-index prefix b0 at its
 // first unit; later units' values follow from these by walking the units in
 // order (split_of).
@@ -147,8 +147,8 @@ struct WgSched {
   int u0, t0, u1, t1, q, c0, b0;
 };
 
-// Splits of a unit of n tiles whose cost interval starts at c, and the
-// first workgroup that holds one (-1 for a unit with no tile).
+// Splits of a unit of n chunks whose cost interval starts at c, and the
+// first workgroup that holds one (-1 for a unit with no chunk).
 __device__ __forceinline__ void unit_splits(int c, int n, int q, int* ns, int* gf) {
   if (n <= 0) {
     *ns = 0;
@@ -186,13 +186,13 @@ __device__ WgSched sched_in_wg(const DecodeArgs& a, int* scr, int tid, int wg) {
     const int per = (U + 63) / 64;
     const int lo = min(U, lane * per), hi = min(U, lo + per);
     int s = 0;
-    for (int u = lo; u < hi; u++) s += unit_tiles(a, SPARSE, u) + kSplitCost;
+    for (int u = lo; u < hi; u++) s += unit_chunks(a, SPARSE, u) + kSplitCost;
     const int incl = wave_incl_scan(s, lane);
     const int total = __shfl(incl, 63, 64);
     int run = incl - s;
     for (int u = lo; u < hi; u++) {
       C[u] = run;
-      run += unit_tiles(a, SPARSE, u) + kSplitCost;
+      run += unit_chunks(a, SPARSE, u) + kSplitCost;
     }
     if (lane == 63) C[U] = total;
     const int q = max((total + G - 1) / G, kMinWgCost);

@@ -32,11 +32,13 @@ constexpr int kBatch = 4;  // splits whose loads are in flight together (8 and 1
 
 template <bool SPARSE>
 __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
-  const int uu = blockIdx.x;
+  // flat grid: consecutive blocks take consecutive 4 KB of one unit's partials
+  const int per_unit = gridDim.x / a.n_units;
+  const int uu = blockIdx.x / per_unit, by = blockIdx.x - uu * per_unit;
   const int ns = a.ws_meta[4 * uu + 2];
   if (ns == 1) return;
   const int t = threadIdx.x;
-  const int blk = blockIdx.y * 8 + (t >> 5);  // fragment block (rb, db, q)
+  const int blk = by * 8 + (t >> 5);  // fragment block (rb, db, q)
   const int j = t & 31;
   const int q = blk & 3, db = (blk >> 2) & 15, rb = blk >> 6;
   const int r = 32 * rb + 2 * (j & 15);       // first of the two rows
@@ -135,7 +137,7 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
 
 hipError_t launch_combine(const Geometry& g, const DecodeArgs& a, hipStream_t stream) {
   // 8 fragment blocks (4 KB of fp16) per 256-thread block, 64 per 32 rows
-  dim3 grid(g.n_units, ((g.m_unit + 31) / 32) * 8);
+  dim3 grid((unsigned)g.n_units * (unsigned)(((g.m_unit + 31) / 32) * 8));
   if (g.sparse)
     hipLaunchKernelGGL(kern::combine_kernel<true>, grid, dim3(256), 0, stream, a);
   else

@@ -21,18 +21,23 @@ struct ProjTile {
   static constexpr int kCols = 32 * 4 / SPLIT;      // columns per workgroup
   static constexpr int kRows = SPLIT > 1 ? 64 : 128;  // rows per row block
   static constexpr int kRowBytes = 2 * K;           // one weight or activation row
-  static constexpr int kWBytes = kCols * kRowBytes; // the weight tile
+  // With the contraction split over the waves, each wave reads its weight
+  // fragment once: it loads it from HBM into registers, and only the
+  // activation tile is staged (so two workgroups fit on a CU).
+  static constexpr bool kWDirect = SPLIT > 1;
+  static constexpr int kWBytes = kWDirect ? 0 : kCols * kRowBytes;  // the weight tile in LDS
   static constexpr int kABytes = kRows * kRowBytes; // the activation tile
   static constexpr int kRedOff = kWBytes + kABytes; // partial tiles of the non-leading waves
   static constexpr int kLdsBytes = kRedOff + (SPLIT > 1 ? 3 * 16 * 64 * 4 : 0);
   static constexpr int kCopies = (kWBytes + kABytes) / 1024;
   static_assert(kRowBytes <= 1024 && 1024 % kRowBytes == 0 && kCopies % 4 == 0, "copy shape");
-  static_assert(kLdsBytes <= 128 * 1024, "LDS budget");
+  static_assert(kLdsBytes <= 80 * 1024, "LDS budget: two workgroups per CU");
 };
 
-// Both tiles are staged in LDS by direct copies of whole rows (1 KB per
-// copy: a weight or activation row is 256 B or 1 KB, contiguous in HBM), so
-// every HBM read is fully coalesced; 16-byte chunk c of tile row r sits at
+// The activation tile (and, without a split contraction, the weight tile)
+// is staged in LDS by direct copies of whole rows (1 KB per copy: a weight
+// or activation row is 256 B or 1 KB, contiguous in HBM), so every such
+// HBM read is fully coalesced; 16-byte chunk c of tile row r sits at
 // position c ^ (r & 15), so that the MFMA operand reads (one chunk of 16
 // consecutive rows per 16 lanes) cover every bank.  `lds` is the dynamic
 // LDS of the launch, ProjTile<K, N, SPLIT>::kLdsBytes bytes.
@@ -44,6 +49,17 @@ __device__ __forceinline__ void head_gemm(const ProjArgs& a, uint8_t* lds, int b
   const int H = a.H, M = a.M;
   const int n_base = bx * T::kCols, m_base = bz * T::kRows;
   constexpr int kChunks = K / 8, kRowsPerCopy = 1024 / T::kRowBytes;
+  const int part = wave % SPLIT;               // which share of the contraction
+  const int col0 = (wave / SPLIT) * 32;        // the wave's columns within the tile
+  constexpr int KS = K / SPLIT / 16;           // k-steps per wave
+  const int kc0 = part * (K / SPLIT / 8);      // first chunk of the wave's share
+  const int wr = col0 + l32;                   // weight tile row of this lane
+  bf16x8 wf[KS];
+  if constexpr (T::kWDirect) {
+    const bf16x8* wp = reinterpret_cast<const bf16x8*>(a.w + ((size_t)h * N + n_base + wr) * K) + kc0 + g;
+#pragma unroll
+    for (int ks = 0; ks < KS; ks++) wf[ks] = wp[2 * ks];
+  }
   {
     int ln = lane;
     asm volatile("" : "+v"(ln));
@@ -69,15 +85,11 @@ __device__ __forceinline__ void head_gemm(const ProjArgs& a, uint8_t* lds, int b
   wait_vm<0>();
   __syncthreads();
 
-  const int part = wave % SPLIT;               // which share of the contraction
-  const int col0 = (wave / SPLIT) * 32;        // the wave's columns within the tile
-  constexpr int KS = K / SPLIT / 16;           // k-steps per wave
-  const int kc0 = part * (K / SPLIT / 8);      // first chunk of the wave's share
-  const int wr = col0 + l32;                   // weight tile row of this lane
-  bf16x8 wf[KS];
+  if constexpr (!T::kWDirect) {
 #pragma unroll
-  for (int ks = 0; ks < KS; ks++)
-    wf[ks] = *reinterpret_cast<const bf16x8*>(lds + wr * T::kRowBytes + (((kc0 + 2 * ks + g) ^ (wr & 15)) << 4));
+    for (int ks = 0; ks < KS; ks++)
+      wf[ks] = *reinterpret_cast<const bf16x8*>(lds + wr * T::kRowBytes + (((kc0 + 2 * ks + g) ^ (wr & 15)) << 4));
+  }
   float* const red = reinterpret_cast<float*>(lds + T::kRedOff);
 #pragma unroll
   for (int mt = 0; mt < T::kRows / 32; mt++) {

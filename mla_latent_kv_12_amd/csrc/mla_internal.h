@@ -23,9 +23,10 @@ constexpr int kTileFp8 = kPage * kBytesFp8Row;    // 36864
 // Scheduling constants, in 32-token chunks (the unit of work of the main
 // pass): a split costs this many chunks of fixed work (its query load, its
 // first chunk without the pipeline, its partial written and read back; 8
-// measured best of 5 to 12), and a workgroup is never given less work.
+// measured best of 5 to 12), and the least work a workgroup is given (one
+// chunk: a small decode is spread over as many workgroups as it has chunks).
 constexpr int kSplitCost = 8;
-constexpr int kMinWgCost = 4;
+constexpr int kMinWgCost = 1;
 // Decodes of up to this many units schedule themselves inside the main pass
 // (its LDS holds the cost prefix); larger ones get a scheduling launch.
 constexpr int kFoldUnits = 2048;

@@ -101,7 +101,7 @@ size_t mla_workspace_size(int B, int Sq, int H, int topk, int num_wg);
 
 /*
  * Split-KV scheduling pass: reads cache_seqlens on the device and writes the
- * work partition (which workgroup processes which 64-token tiles of which
+ * work partition (which workgroup processes which 32-token chunks of which
  * sequence, and where each partial result goes) into the workspace.  It is
  * what mla_decode / mla_sparse_decode run first when `planned` is 0.  Run it
  * once per decode step and pass planned = 1 to every layer's call to reuse
@@ -171,7 +171,7 @@ mla_status mla_sparse_decode(const void *q_nope, const void *q_rope, const void 
  * The three stages that mla_decode / mla_sparse_decode run, for callers that
  * schedule them separately (e.g. to time or overlap them):
  *   mla_plan     split-KV partition (above)
- *   mla_attend   the main pass: streams every 64-token tile of every
+ *   mla_attend   the main pass: streams every 32-token chunk of every
  *                sequence once from HBM and computes softmax attention over
  *                it for all query rows of that sequence; writes out/lse of
  *                sequences that one workgroup finished alone, and partial

@@ -120,7 +120,10 @@ mla_status mla_plan(const int32_t *cache_seqlens, int B, int Sq, int H, int topk
  *   causal        nonzero: query s sees tokens j <= L_b - Sq + s
  *   planned       nonzero: mla_plan already filled this workspace
  * Limits: 1 <= Sq*H; sequences with Sq*H > 128 rows are processed as
- * several 128-row blocks, each reading the cache once.
+ * several 128-row blocks, each reading the cache once.  The schedule counts
+ * work in 32-bit units of 32 tokens: each row block's sequence is cut to
+ * (2^31 - 2^17) / (row blocks of the whole decode) - 8 chunks of 32 tokens
+ * (past 6e10 tokens in all, far beyond any cache that fits in memory).
  * Alignment: q_nope, q_rope, kv_pages, kv_scales, out 16 B; workspace 256 B.
  */
 mla_status mla_decode(const void *q_nope, const void *q_rope, const void *kv_pages,

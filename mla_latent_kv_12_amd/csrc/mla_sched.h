@@ -9,11 +9,16 @@
 namespace mla {
 namespace kern {
 
+// A unit's 32-token chunks, at most (2^31 - 2^17) / n_units - kSplitCost of
+// them, so that the schedule's 32-bit cost arithmetic (the prefix plus up to
+// 2^16 workgroups) cannot overflow whatever lengths the caller passes (the
+// bound is past 6e10 tokens in all).
 __device__ __forceinline__ int unit_chunks(const DecodeArgs& a, bool sparse, int u) {
-  if (sparse) return (a.topk + 31) / 32;
+  const int cap = (0x7fffffff - (1 << 17)) / a.n_units - kSplitCost;
+  if (sparse) return min((a.topk - 1) / 32 + 1, cap);
   int su = u / a.row_blocks;
   int L = ldc(a.seqlens + su);
-  return L > 0 ? (L + 31) / 32 : 0;
+  return L > 0 ? min((L - 1) / 32 + 1, cap) : 0;
 }
 
 struct UnitInfo {

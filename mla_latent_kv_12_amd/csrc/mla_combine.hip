@@ -30,11 +30,9 @@
 namespace mla {
 namespace kern {
 
-namespace {
-constexpr int kBatch = 4;  // splits whose loads are in flight together (8 and 16 measured slower)
-}
-
-template <bool SPARSE, int SG>
+// kBatch: splits whose loads a thread keeps in flight together (4, or 8
+// when its group can be expected to walk at least 8 splits).
+template <bool SPARSE, int SG, int kBatch>
 __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   // Flat grid, a unit's blocks consecutive, so that blocks dispatched
   // together read consecutive 4 KB of the same partials.  A block covers F
@@ -186,26 +184,29 @@ hipError_t launch_combine(const Geometry& g, const DecodeArgs& a, hipStream_t st
   // Thread groups per unit from the splits a unit can be expected to have
   // (the workgroups shared over the units, plus one): a long chain of splits
   // is shared out among the groups instead of walked by each thread alone
-  // (up to 16 splits one group measured faster).
+  // (up to 16 splits one group measured faster); 8 loads in flight per
+  // thread when its group can be expected to walk 8 splits or more.
   const int est = (g.num_wg + g.n_units - 1) / g.n_units + 1;
   const int sg = est > 32 ? 8 : est > 16 ? 4 : 1;
+  const bool deep = est >= 8 * sg;
   // a unit has 64 fragment blocks (4 KB of fp16 each) per 32 rows; a
   // 256-thread block covers 8 / sg of them
   const dim3 grid((unsigned)g.n_units * (unsigned)(((g.m_unit + 31) / 32) * 8 * sg));
   auto go = [&](auto SPARSE, auto SG) {
-    hipLaunchKernelGGL((kern::combine_kernel<decltype(SPARSE)::value, decltype(SG)::value>), grid, dim3(256), 0,
-                       stream, a);
+    constexpr bool sp = decltype(SPARSE)::value;
+    constexpr int gs = decltype(SG)::value;
+    if (deep)
+      hipLaunchKernelGGL((kern::combine_kernel<sp, gs, 8>), grid, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((kern::combine_kernel<sp, gs, 4>), grid, dim3(256), 0, stream, a);
   };
-  using T = std::true_type;
-  using F = std::false_type;
-  using I1 = std::integral_constant<int, 1>;
-  using I4 = std::integral_constant<int, 4>;
-  using I8 = std::integral_constant<int, 8>;
-  if (g.sparse) {
-    if (sg == 8) go(T{}, I8{}); else if (sg == 4) go(T{}, I4{}); else go(T{}, I1{});
-  } else {
-    if (sg == 8) go(F{}, I8{}); else if (sg == 4) go(F{}, I4{}); else go(F{}, I1{});
-  }
+  auto by_groups = [&](auto SPARSE) {
+    if (sg == 8) go(SPARSE, std::integral_constant<int, 8>{});
+    else if (sg == 4) go(SPARSE, std::integral_constant<int, 4>{});
+    else go(SPARSE, std::integral_constant<int, 1>{});
+  };
+  if (g.sparse) by_groups(std::true_type{});
+  else by_groups(std::false_type{});
   return hipGetLastError();
 }
 
